@@ -1,0 +1,262 @@
+// C-ABI of the i8mm library: argument validation, workspace layout and the
+// launch sequence of each entry point. Declarations and the contract of each
+// call are in include/i8mm.h.
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/i8mm.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return I8MM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(I8MM_ENODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 1) return I8MM_OK;
+    if (st == 2) return fail(I8MM_ENODEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(I8MM_ENODEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < kMaxDevices) g_dev_state[dev].store(good ? 1 : 2, std::memory_order_release);
+  if (!good) return fail(I8MM_ENODEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return I8MM_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(I8MM_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return I8MM_OK;
+}
+
+#define I8MM_TRY(expr)        \
+  do {                        \
+    int _st = (expr);         \
+    if (_st != I8MM_OK) return _st; \
+  } while (0)
+
+// Common shape checks: sizes non-negative and within int32 row/column counts,
+// K a multiple of 16 and within the int32 accumulation bound.
+int check_dims(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(I8MM_EINVAL, "%s: negative size", fn);
+  if (M > INT32_MAX || N > INT32_MAX) return fail(I8MM_EINVAL, "%s: size beyond int32", fn);
+  if (K % 16 != 0) return fail(I8MM_EALIGN, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (K > I8MM_MAX_K) return fail(I8MM_ERANGE, "%s: K=%lld exceeds %d", fn, (long long)K, I8MM_MAX_K);
+  return I8MM_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, bool required) {
+  if (!p) return required ? fail(I8MM_EINVAL, "%s: %s is NULL", fn, name) : I8MM_OK;
+  if (!aligned16(p)) return fail(I8MM_EALIGN, "%s: %s is not 16-byte aligned", fn, name);
+  return I8MM_OK;
+}
+
+constexpr int64_t kAlign = 256;
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Workspace of linear_int8_mixed: bitmap | cols | n | sx | Xq | Xo.
+bool layout(int64_t M, int64_t K, int64_t* off) {
+  if (M < 0 || K < 0 || K % 16 != 0 || K > I8MM_MAX_K || M > INT32_MAX) return false;
+  int64_t p = 0;
+  off[0] = p; p = round_up(p + (K + 31) / 32 * 4, kAlign);
+  off[1] = p; p = round_up(p + K * 4, kAlign);
+  off[2] = p; p = round_up(p + 4, kAlign);
+  off[3] = p; p = round_up(p + M * 4, kAlign);
+  off[4] = p; p = round_up(p + M * K, kAlign);
+  off[5] = p; p = round_up(p + M * I8MM_OUTLIER_LD(K) * 2, kAlign);
+  off[6] = p;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* i8mm_last_error(void) { return g_err; }
+
+const char* i8mm_status_string(int status) {
+  switch (status) {
+    case I8MM_OK: return "I8MM_OK";
+    case I8MM_EINVAL: return "I8MM_EINVAL";
+    case I8MM_EALIGN: return "I8MM_EALIGN";
+    case I8MM_EWORKSPACE: return "I8MM_EWORKSPACE";
+    case I8MM_ENODEVICE: return "I8MM_ENODEVICE";
+    case I8MM_ELAUNCH: return "I8MM_ELAUNCH";
+    case I8MM_ERANGE: return "I8MM_ERANGE";
+    default: return "I8MM_UNKNOWN";
+  }
+}
+
+size_t linear_int8_mixed_workspace_bytes(int64_t M, int64_t K) {
+  int64_t off[7];
+  return layout(M, K, off) ? (size_t)off[6] : 0;
+}
+
+int i8mm_workspace_offsets(int64_t M, int64_t K, int64_t* offsets) {
+  if (!offsets) return fail(I8MM_EINVAL, "i8mm_workspace_offsets: offsets is NULL");
+  if (!layout(M, K, offsets)) return fail(I8MM_EINVAL, "i8mm_workspace_offsets: invalid sizes");
+  return ok();
+}
+
+int int8_quantize_colwise_weight(const uint16_t* W, int64_t N, int64_t K, int8_t* Wq, float* sw,
+                                 i8mm_stream_t stream) {
+  const char* fn = "int8_quantize_colwise_weight";
+  I8MM_TRY(check_dims(fn, N, 0, K));
+  I8MM_TRY(check_ptr(fn, "W", W, true));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
+  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  if (N == 0) return ok();
+  I8MM_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  I8MM_TRY(launched(i8mm::launch_rows(W, N, K, nullptr, Wq, sw, nullptr, nullptr, nullptr, s), fn));
+  return ok();
+}
+
+int int8_quantize_rowwise(const uint16_t* X, int64_t M, int64_t K, const uint32_t* outlier_bitmap,
+                          int8_t* Xq, float* sx, i8mm_stream_t stream) {
+  const char* fn = "int8_quantize_rowwise";
+  I8MM_TRY(check_dims(fn, M, 0, K));
+  I8MM_TRY(check_ptr(fn, "X", X, true));
+  I8MM_TRY(check_ptr(fn, "outlier_bitmap", outlier_bitmap, false));
+  I8MM_TRY(check_ptr(fn, "Xq", Xq, true));
+  I8MM_TRY(check_ptr(fn, "sx", sx, true));
+  if (M == 0) return ok();
+  I8MM_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  I8MM_TRY(launched(
+      i8mm::launch_rows(X, M, K, outlier_bitmap, Xq, sx, nullptr, nullptr, nullptr, s), fn));
+  return ok();
+}
+
+int outlier_detect_gather(const uint16_t* X, int64_t M, int64_t K, float threshold,
+                          uint32_t* bitmap, int32_t* cols, int32_t* n_outliers, uint16_t* Xo,
+                          i8mm_stream_t stream) {
+  const char* fn = "outlier_detect_gather";
+  I8MM_TRY(check_dims(fn, M, 0, K));
+  if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
+  I8MM_TRY(check_ptr(fn, "X", X, M > 0));
+  I8MM_TRY(check_ptr(fn, "bitmap", bitmap, true));
+  I8MM_TRY(check_ptr(fn, "cols", cols, true));
+  I8MM_TRY(check_ptr(fn, "n_outliers", n_outliers, true));
+  I8MM_TRY(check_ptr(fn, "Xo", Xo, false));
+  I8MM_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nwords = (K + 31) / 32;
+  I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
+  if (M > 0) I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, threshold, bitmap, s), fn));
+  I8MM_TRY(launched(i8mm::launch_cols_from_bitmap(bitmap, K, cols, n_outliers, s), fn));
+  if (Xo && M > 0)
+    I8MM_TRY(launched(
+        i8mm::launch_rows(X, M, K, bitmap, nullptr, nullptr, Xo, nullptr, nullptr, s), fn));
+  return ok();
+}
+
+int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
+                    int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
+                    const int32_t* n_outliers, const uint16_t* bias, uint16_t* Y, int32_t* C,
+                    i8mm_stream_t stream) {
+  const char* fn = "int8_mm_dequant";
+  I8MM_TRY(check_dims(fn, M, N, K));
+  I8MM_TRY(check_ptr(fn, "Xq", Xq, true));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
+  I8MM_TRY(check_ptr(fn, "sx", sx, true));
+  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  const bool any_o = Xo || cols || n_outliers;
+  const bool all_o = Xo && cols && n_outliers;
+  if (any_o && !all_o)
+    return fail(I8MM_EINVAL, "%s: Xo, cols and n_outliers must be given together", fn);
+  I8MM_TRY(check_ptr(fn, "Xo", Xo, false));
+  I8MM_TRY(check_ptr(fn, "cols", cols, false));
+  I8MM_TRY(check_ptr(fn, "n_outliers", n_outliers, false));
+  I8MM_TRY(check_ptr(fn, "bias", bias, false));
+  I8MM_TRY(check_ptr(fn, "Y", Y, false));
+  I8MM_TRY(check_ptr(fn, "C", C, false));
+  if (!Y && !C) return fail(I8MM_EINVAL, "%s: neither Y nor C given", fn);
+  if (M == 0 || N == 0) return ok();
+  I8MM_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  I8MM_TRY(launched(
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, s), fn));
+  return ok();
+}
+
+int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                      int64_t N, const uint16_t* bias, float threshold, uint16_t* Y,
+                      void* workspace, size_t workspace_bytes, i8mm_stream_t stream) {
+  const char* fn = "linear_int8_mixed";
+  I8MM_TRY(check_dims(fn, M, N, K));
+  if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
+  I8MM_TRY(check_ptr(fn, "X", X, true));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
+  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  I8MM_TRY(check_ptr(fn, "bias", bias, false));
+  I8MM_TRY(check_ptr(fn, "Y", Y, true));
+  int64_t off[7];
+  layout(M, K, off);
+  if (!workspace) return fail(I8MM_EWORKSPACE, "%s: workspace is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(I8MM_EALIGN, "%s: workspace is not 256-byte aligned", fn);
+  if ((int64_t)workspace_bytes < off[6])
+    return fail(I8MM_EWORKSPACE, "%s: workspace has %zu bytes, needs %lld", fn, workspace_bytes,
+                (long long)off[6]);
+  if (M == 0 || N == 0) return ok();
+  I8MM_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + off[0]);
+  int32_t* cols = reinterpret_cast<int32_t*>(ws + off[1]);
+  int32_t* n_o = reinterpret_cast<int32_t*>(ws + off[2]);
+  float* sx = reinterpret_cast<float*>(ws + off[3]);
+  int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
+  uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
+  const int64_t nwords = (K + 31) / 32;
+  I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
+  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, threshold, bitmap, s), fn));
+  I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+  I8MM_TRY(launched(
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, s), fn));
+  return ok();
+}
+
+int i8mm_gelu_f16(const uint16_t* X, int64_t count, uint16_t* Y, i8mm_stream_t stream) {
+  const char* fn = "i8mm_gelu_f16";
+  if (count < 0) return fail(I8MM_EINVAL, "%s: negative count", fn);
+  I8MM_TRY(check_ptr(fn, "X", X, true));
+  I8MM_TRY(check_ptr(fn, "Y", Y, true));
+  if (count == 0) return ok();
+  I8MM_TRY(check_device());
+  I8MM_TRY(launched(i8mm::launch_gelu(X, count, Y, (hipStream_t)stream), fn));
+  return ok();
+}
+
+}  // extern "C"

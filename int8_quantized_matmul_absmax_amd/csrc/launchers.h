@@ -1,0 +1,33 @@
+// Internal launch wrappers of the i8mm kernels. Arguments are validated by
+// the C-ABI layer before these are called; each returns the hipError_t of its
+// launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
+
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau,
+                                uint32_t* bitmap, hipStream_t s);
+
+hipError_t launch_cols_from_bitmap(const uint32_t* bitmap, int64_t K, int32_t* cols,
+                                   int32_t* n_out, hipStream_t s);
+
+// Row pass over X (or W): optional absmax quantization (Xq, sx), optional
+// gather of outlier columns (Xo), optional cols/n output from the first row's
+// block. bitmap == nullptr means no outlier columns.
+hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* bitmap,
+                       int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
+                       hipStream_t s);
+
+hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
+                       int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
+                       const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
+                       uint16_t* Y, int32_t* C, hipStream_t s);
+
+hipError_t launch_gelu(const uint16_t* X, int64_t count, uint16_t* Y, hipStream_t s);
+
+}  // namespace i8mm

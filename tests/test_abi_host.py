@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+The library must load, export every symbol include/i8mm.h declares, and reject
+invalid arguments on the host with the documented status before touching a
+device. Fake device addresses are used only where validation fails first.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import int8_quantized_matmul_absmax_amd as i8
+from int8_quantized_matmul_absmax_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "i8mm.h")
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)    # not 16-byte aligned
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return i8.ensure_built()
+
+
+def _declared_names():
+    src = open(HEADER).read()
+    return set(re.findall(r"I8MM_API\s+[\w\s\*]+?\b(\w+)\s*\(", src))
+
+
+def test_header_and_exports_agree(lib):
+    names = _declared_names()
+    assert names == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_only_the_abi_is_exported(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_lib.EXPORTS) <= syms
+    assert not [s for s in syms if "i8mm" in s and s not in _lib.EXPORTS and s.startswith("_Z")]
+
+
+def test_status_strings(lib):
+    assert lib.i8mm_status_string(0) == b"I8MM_OK"
+    assert lib.i8mm_status_string(-3) == b"I8MM_EWORKSPACE"
+    assert lib.i8mm_status_string(99) == b"I8MM_UNKNOWN"
+
+
+def test_workspace_layout_is_pure_and_consistent(lib):
+    for M, K in [(1, 16), (16, 256), (2048, 4096), (4096, 12288), (0, 64)]:
+        off = (ctypes.c_int64 * 7)()
+        assert lib.i8mm_workspace_offsets(M, K, off) == 0
+        off = list(off)
+        assert off[0] == 0 and all(b >= a for a, b in zip(off, off[1:]))
+        assert all(o % 256 == 0 for o in off)
+        assert off[1] - off[0] >= (K + 31) // 32 * 4
+        assert off[2] - off[1] >= 4 * K
+        assert off[4] - off[3] >= 4 * M
+        assert off[5] - off[4] >= M * K
+        assert off[6] - off[5] >= M * ((K + 31) // 32 * 32) * 2
+        assert lib.linear_int8_mixed_workspace_bytes(M, K) == off[6]
+    assert lib.linear_int8_mixed_workspace_bytes(4, 20) == 0
+    assert lib.linear_int8_mixed_workspace_bytes(-1, 16) == 0
+    assert lib.i8mm_workspace_offsets(4, 16, None) == _lib.I8MM_EINVAL
+
+
+def test_validation_quantize_weight(lib):
+    f = lib.int8_quantize_colwise_weight
+    assert f(NUL, 4, 16, A, A2, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, NUL, A2, NUL) == _lib.I8MM_EINVAL
+    assert f(A, -1, 16, A, A2, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 24, A, A2, NUL) == _lib.I8MM_EALIGN
+    assert f(MIS, 4, 16, A, A2, NUL) == _lib.I8MM_EALIGN
+    kmax16 = _lib.I8MM_MAX_K // 16 * 16          # largest valid K (multiple of 16)
+    assert f(A, 4, kmax16 + 16, A, A2, NUL) == _lib.I8MM_ERANGE
+    assert f(A, 4, kmax16, NUL, A2, NUL) == _lib.I8MM_EINVAL    # K itself accepted
+    assert f(A, 0, 16, A, A2, NUL) == _lib.I8MM_OK              # empty: no-op
+
+
+def test_validation_last_error_text(lib):
+    assert lib.int8_quantize_colwise_weight(A, 4, 24, A, A2, NUL) == _lib.I8MM_EALIGN
+    assert b"multiple of 16" in lib.i8mm_last_error()
+
+
+def test_validation_rowwise(lib):
+    f = lib.int8_quantize_rowwise
+    assert f(NUL, 4, 16, NUL, A, A2, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, MIS, A, A2, NUL) == _lib.I8MM_EALIGN
+    assert f(A, 4, 8, NUL, A, A2, NUL) == _lib.I8MM_EALIGN
+    assert f(A, 0, 16, NUL, A, A2, NUL) == _lib.I8MM_OK
+
+
+def test_validation_outlier_detect(lib):
+    f = lib.outlier_detect_gather
+    assert f(A, 4, 16, math.nan, A, A, A, NUL, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, 6.0, NUL, A, A, NUL, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, 6.0, A, NUL, A, NUL, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, 6.0, A, A, NUL, NUL, NUL) == _lib.I8MM_EINVAL
+    assert f(A, 4, 16, 6.0, A, A, A, MIS, NUL) == _lib.I8MM_EALIGN
+    assert f(A, 4, 40, 6.0, A, A, A, NUL, NUL) == _lib.I8MM_EALIGN
+
+
+def test_validation_mm_dequant(lib):
+    f = lib.int8_mm_dequant
+    ok = [A, A, A, A, 4, 4, 16, NUL, NUL, NUL, NUL, A, NUL, NUL]
+    bad = list(ok); bad[0] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(ok); bad[7] = A           # Xo without cols / n
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(ok); bad[11] = NUL        # neither Y nor C
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(ok); bad[10] = MIS        # misaligned bias
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(ok); bad[6] = 17
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(ok); bad[5] = -2
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(ok); bad[4] = 0           # M == 0: no-op
+    assert f(*bad) == _lib.I8MM_OK
+
+
+def test_validation_linear(lib):
+    f = lib.linear_int8_mixed
+    M, K, N = 8, 64, 32
+    need = lib.linear_int8_mixed_workspace_bytes(M, K)
+    ws = ctypes.c_void_p(0x100000)
+    args = [A, M, K, A, A, N, NUL, 6.0, A2, ws, need, NUL]
+    bad = list(args); bad[10] = need - 1
+    assert f(*bad) == _lib.I8MM_EWORKSPACE
+    bad = list(args); bad[9] = NUL
+    assert f(*bad) == _lib.I8MM_EWORKSPACE
+    bad = list(args); bad[9] = ctypes.c_void_p(0x100010)     # 16- but not 256-aligned
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(args); bad[7] = math.nan
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[8] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[2] = 72
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(args); bad[1] = 0; bad[10] = lib.linear_int8_mixed_workspace_bytes(0, K)
+    assert f(*bad) == _lib.I8MM_OK
+
+
+def test_validation_gelu(lib):
+    assert lib.i8mm_gelu_f16(A, -1, A, NUL) == _lib.I8MM_EINVAL
+    assert lib.i8mm_gelu_f16(MIS, 4, A, NUL) == _lib.I8MM_EALIGN
+    assert lib.i8mm_gelu_f16(A, 0, A, NUL) == _lib.I8MM_OK
+
+
+def test_no_gfx950_device_is_reported(lib):
+    """Without a gfx950 GPU, a valid call fails loudly with ENODEVICE and
+    launches nothing (the product path has no CPU fallback)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the no-device path is not reachable")
+    st = lib.int8_quantize_colwise_weight(A, 4, 16, A, A2, NUL)
+    assert st == _lib.I8MM_ENODEVICE
+
+
+def test_python_ops_refuse_cpu_tensors():
+    import torch
+    W = torch.zeros((4, 16), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        i8.ops.int8_quantize_colwise_weight(W)
+    with pytest.raises(TypeError):
+        i8.ops.int8_quantize_colwise_weight(W.float())

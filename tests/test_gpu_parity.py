@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: int8 codes, absmax scales, outlier bitmap / column list / count,
+gathered outlier columns, int32 accumulators. Tolerance: fp16 outputs within
+max |dY| / max |Y_ref| <= 1e-3 of the oracle's fp64 value.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from int8_quantized_matmul_absmax_amd import synth
+from oracle import llm_int8 as O
+from tests.gpu_helpers import Y_TOL, bitmap_u32, dev, host, note, sample_rows, y_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops(gpu):
+    return gpu.ops
+
+
+# ------------------------------------------------------------------ a4: weight
+
+@pytest.mark.parametrize("shape", [(256, 256), (1000, 4112), (64, 16), (33, 12288), (7, 32)])
+def test_weight_quant_bitexact(gpu, shape):
+    N, K = shape
+    note("weight quant %s" % (shape,))
+    rng = np.random.default_rng(N * 7 + K)
+    W = synth.normal_f16(rng, (N, K), 0.02)
+    W[min(3, N - 1), :] = 0                       # an all-zero row
+    Wq_ref, sw_ref = O.quantize_weight_rows(W)
+    Wq, sw = _ops(gpu).int8_quantize_colwise_weight(dev(W))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+
+
+def test_weight_quant_ties(gpu):
+    note("weight quant ties")
+    W = np.zeros((2, 16), np.float16)
+    W[0, :4] = [127.0, 2.5, 0.5, -3.5]            # scale 1: 2.5 -> 2, -3.5 -> -4
+    W[1, :3] = [np.float16(127 / 32), 0.078125, 0.109375]   # scale 32: 2.5 -> 2, 3.5 -> 4
+    Wq, sw = _ops(gpu).int8_quantize_colwise_weight(dev(W))
+    assert host(Wq)[0, :4].tolist() == [127, 2, 0, -4]
+    assert host(Wq)[1, :3].tolist() == [127, 2, 4]
+    Wq_ref, _ = O.quantize_weight_rows(W)
+    assert np.array_equal(host(Wq), Wq_ref)
+
+
+# ------------------------------------------------------------------ a1, a2: detection
+
+def _check_detect(gpu, X, tau):
+    M, K = X.shape
+    cols_ref = O.detect_outlier_columns(X, tau)
+    n_ref = cols_ref.size
+    bitmap, cols, n, Xo = _ops(gpu).outlier_detect_gather(dev(X), tau)
+    torch.cuda.synchronize()
+    assert int(host(n)[0]) == n_ref
+    assert np.array_equal(bitmap_u32(bitmap), O.outlier_bitmap(cols_ref, K))
+    assert np.array_equal(host(cols)[:n_ref], cols_ref)
+    ld = _ops(gpu).outlier_ld(n_ref)
+    Xo_h = host(Xo)[: M * ld].reshape(M, ld) if M else np.zeros((0, ld), np.float16)
+    assert np.array_equal(Xo_h[:, :n_ref].view(np.uint16), X[:, cols_ref].view(np.uint16))
+    assert np.all(Xo_h[:, n_ref:].view(np.uint16) == 0)
+    return cols_ref
+
+
+@pytest.mark.parametrize("case", ["tiny", "planted_ragged", "single_row", "many_outliers"])
+def test_outlier_detect_gather(gpu, case):
+    note("detect %s" % case)
+    if case == "tiny":
+        X = synth.tiny()["X"]
+    elif case == "planted_ragged":
+        X = synth.opt_ffn_up(M=300, K=4112, N=16)["X"]
+    elif case == "single_row":
+        X = synth.decode(1)["X"]
+    else:
+        rng = np.random.default_rng(21)
+        X = synth.normal_f16(rng, (37, 1040), 1.0)
+        synth.plant_outlier_columns(rng, X, 100, 6.0, 9.0, 0.1)
+    cols = _check_detect(gpu, X, 6.0)
+    assert cols.size >= 1
+
+
+def test_outlier_threshold_edges(gpu):
+    note("detect edges")
+    rng = np.random.default_rng(5)
+    X = synth.normal_f16(rng, (9, 160), 1.0)
+    X = np.clip(X.astype(np.float32), -5.5, 5.5).astype(np.float16)
+    X[4, 13] = 6.0                     # exactly tau: outlier (>=)
+    X[2, 140] = -6.0
+    X[0, 15] = np.float16(5.99609375)  # just below: not an outlier
+    cols = _check_detect(gpu, X, 6.0)
+    assert cols.tolist() == [13, 140]
+    assert _check_detect(gpu, X, float("inf")).size == 0
+    assert _check_detect(gpu, X, 0.0).size == 160
+    assert _check_detect(gpu, X, -1.0).size == 160
+
+
+def test_outlier_detect_empty_rows(gpu):
+    note("detect M=0")
+    X = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    bitmap, cols, n, Xo = _ops(gpu).outlier_detect_gather(X, 6.0)
+    torch.cuda.synchronize()
+    assert int(host(n)[0]) == 0 and np.all(host(bitmap) == 0)
+
+
+# ------------------------------------------------------------------ a3: rows of X
+
+@pytest.mark.parametrize("case", ["tiny", "medium", "no_bitmap"])
+def test_rowwise_quant_bitexact(gpu, case):
+    note("rowwise %s" % case)
+    if case == "tiny":
+        X = synth.tiny()["X"]
+    else:
+        X = synth.opt_ffn_up(M=257, K=4096, N=16)["X"]
+    X[1, :] = 0
+    if case == "no_bitmap":
+        cols = np.zeros(0, np.int32)
+        bm = None
+    else:
+        cols = O.detect_outlier_columns(X, 6.0)
+        bm = dev(O.outlier_bitmap(cols, X.shape[1]).view(np.int32))
+    Xq_ref, sx_ref = O.quantize_activation_rows(X, cols)
+    Xq, sx = _ops(gpu).int8_quantize_rowwise(dev(X), bm)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Xq), Xq_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ a5: int32 GEMM
+
+@pytest.mark.parametrize("mnk", [(1, 1, 16), (7, 50, 48), (130, 260, 272), (300, 1000, 4112),
+                                 (16, 4096, 4096), (256, 384, 1024)])
+def test_int32_accumulators_bitexact(gpu, mnk):
+    M, N, K = mnk
+    note("int32 gemm %s" % (mnk,))
+    Xq = synth.random_codes(M + 1, (M, K))
+    Wq = synth.random_codes(N + 2, (N, K))
+    C_ref = O.int32_accumulators(Xq, Wq)
+    sx = np.ones(M, np.float32)
+    sw = np.ones(N, np.float32)
+    C = _ops(gpu).int8_mm_dequant(dev(Xq), dev(Wq), dev(sx), dev(sw), want_y=False,
+                                  want_int32=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(C), C_ref)
+
+
+def test_int32_accumulators_extremes(gpu):
+    note("int32 gemm extremes")
+    M, N, K = 64, 96, 8192
+    Xq = np.full((M, K), 127, np.int8)
+    Xq[1::2] = -127
+    Wq = np.full((N, K), -127, np.int8)
+    C = _ops(gpu).int8_mm_dequant(dev(Xq), dev(Wq), dev(np.ones(M, np.float32)),
+                                  dev(np.ones(N, np.float32)), want_y=False, want_int32=True)
+    C_ref = O.int32_accumulators(Xq, Wq)
+    assert np.array_equal(host(C), C_ref)
+    assert int(np.abs(C_ref).max()) == K * 127 * 127
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _run_linear(gpu, X, Wq_ref, sw_ref, tau=6.0, bias=None):
+    """GPU layer from the oracle's own quantized weight (uploaded), returns
+    (Y, workspace views)."""
+    ops = _ops(gpu)
+    M, K = X.shape
+    ws = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    Y = ops.linear_int8_mixed(dev(X), dev(Wq_ref), dev(sw_ref),
+                              None if bias is None else dev(bias), tau, ws)
+    torch.cuda.synchronize()
+    return host(Y), ops.workspace_views(ws, M, K)
+
+
+def _check_intermediates(gpu, views, X, ref):
+    M, K = X.shape
+    n = ref["n"]
+    assert int(host(views["n"])[0]) == n
+    assert np.array_equal(host(views["cols"])[:n], ref["cols"])
+    assert np.array_equal(host(views["bitmap"]).view(np.uint32), O.outlier_bitmap(ref["cols"], K))
+    assert np.array_equal(host(views["Xq"]), ref["Xq"])
+    assert np.array_equal(host(views["sx"]).view(np.uint32), ref["sx"].view(np.uint32))
+    ld = _ops(gpu).outlier_ld(n)
+    Xo = host(views["Xo"])[: M * ld].reshape(M, ld)
+    assert np.array_equal(Xo[:, :n].view(np.uint16), X[:, ref["cols"]].view(np.uint16))
+
+
+@pytest.mark.parametrize("case", ["tiny", "decode1", "decode4", "decode16", "medium_ragged",
+                                  "bias"])
+def test_linear_full_oracle(gpu, case):
+    note("linear %s" % case)
+    if case == "tiny":
+        d = synth.tiny()
+    elif case.startswith("decode"):
+        d = synth.decode(int(case[6:]))
+    elif case == "medium_ragged":
+        d = synth.opt_ffn_up(M=300, K=4112, N=1000)
+    else:
+        d = synth.opt_ffn_up(M=130, K=1024, N=520)
+    X, W = d["X"], d["W"]
+    Wq, sw = O.quantize_weight_rows(W)
+    bias = None
+    if case == "bias":
+        bias = synth.normal_f16(np.random.default_rng(3), (W.shape[0],), 0.5)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0, bias)
+    Y, views = _run_linear(gpu, X, Wq, sw, 6.0, bias)
+    _check_intermediates(gpu, views, X, ref)
+    assert set(d["planted"].tolist()) <= set(ref["cols"].tolist())
+    err = y_err(Y, ref["Y"])
+    assert err <= Y_TOL, err
+    # the dequantized int8 part and the fp16 part both matter on these inputs
+    assert np.abs(ref["Yo"]).max() > 0
+
+
+@pytest.mark.parametrize("case", ["tau_zero_all_outliers", "tau_inf_none", "n17", "n33",
+                                  "exact_threshold", "zero_rows", "k16", "three_d"])
+def test_linear_edge_cases(gpu, case):
+    note("linear edge %s" % case)
+    rng = np.random.default_rng(17)
+    tau = 6.0
+    if case == "k16":
+        X = synth.normal_f16(rng, (5, 16), 2.0)
+        W = synth.normal_f16(rng, (70, 16), 0.1)
+    else:
+        X = synth.normal_f16(rng, (70, 512), 1.0)
+        W = synth.normal_f16(rng, (150, 512), 0.05)
+    if case == "tau_zero_all_outliers":
+        tau = 0.0
+    elif case == "tau_inf_none":
+        tau = float("inf")
+    elif case in ("n17", "n33"):
+        synth.plant_outlier_columns(rng, X, int(case[1:]), 7.0, 30.0, 0.3)
+    elif case == "exact_threshold":
+        X = np.clip(X.astype(np.float32), -5.0, 5.0).astype(np.float16)
+        X[3, 100] = 6.0
+        X[10, 7] = -6.0
+    elif case == "zero_rows":
+        X[0, :] = 0
+        X[5, :] = 0
+        X[5, 9] = 20.0
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, tau)
+    if case == "three_d":
+        ops = _ops(gpu)
+        Y3 = ops.linear_int8_mixed(dev(X).reshape(7, 10, 512), dev(Wq), dev(sw), None, tau)
+        torch.cuda.synchronize()
+        assert tuple(Y3.shape) == (7, 10, 150)
+        assert y_err(host(Y3).reshape(70, 150), ref["Y"]) <= Y_TOL
+        return
+    Y, views = _run_linear(gpu, X, Wq, sw, tau)
+    _check_intermediates(gpu, views, X, ref)
+    assert y_err(Y, ref["Y"]) <= Y_TOL
+    if case == "tau_zero_all_outliers":
+        assert ref["n"] == X.shape[1]
+    if case == "exact_threshold":
+        assert ref["cols"].tolist() == [7, 100]
+    if case in ("n17", "n33"):
+        assert ref["n"] >= int(case[1:])
+
+
+def test_linear_is_deterministic(gpu):
+    note("determinism")
+    d = synth.opt_ffn_up(M=200, K=1024, N=700)
+    Wq, sw = O.quantize_weight_rows(d["W"])
+    Y1, _ = _run_linear(gpu, d["X"], Wq, sw)
+    Y2, _ = _run_linear(gpu, d["X"], Wq, sw)
+    assert np.array_equal(Y1.view(np.uint16), Y2.view(np.uint16))
+
+
+def test_mm_dequant_matches_linear(gpu):
+    """The step-level calls composed by hand give the same bits as the fused call."""
+    note("composed steps")
+    d = synth.opt_ffn_up(M=96, K=1024, N=384)
+    ops = _ops(gpu)
+    X = dev(d["X"])
+    Wq, sw = ops.int8_quantize_colwise_weight(dev(d["W"]))
+    bitmap, cols, n, Xo = ops.outlier_detect_gather(X, 6.0)
+    Xq, sx = ops.int8_quantize_rowwise(X, bitmap)
+    Y1 = ops.int8_mm_dequant(Xq, Wq, sx, sw, Xo, cols, n)
+    Y2 = ops.linear_int8_mixed(X, Wq, sw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Y1).view(np.uint16), host(Y2).view(np.uint16))
+
+
+def test_int8_linear_module(gpu):
+    note("Int8Linear")
+    d = synth.tiny()
+    lin = gpu.Int8Linear(256, 256)
+    lin.quantize_(dev(d["W"]))
+    with pytest.raises(RuntimeError):
+        lin.quantize_(dev(d["W"]))
+    Wq_ref, sw_ref = O.quantize_weight_rows(d["W"])
+    assert np.array_equal(host(lin.CB), Wq_ref)
+    Y = lin(dev(d["X"]))
+    torch.cuda.synchronize()
+    ref = O.linear_int8_mixed(d["X"], Wq_ref, sw_ref)
+    assert y_err(host(Y), ref["Y"]) <= Y_TOL
+    with pytest.raises(TypeError):
+        lin(dev(d["X"]).float())
+
+
+def test_gelu(gpu):
+    note("gelu")
+    rng = np.random.default_rng(8)
+    X = synth.normal_f16(rng, (4099,), 3.0)
+    Y = host(_ops(gpu).gelu_f16(dev(X)))
+    ref = O.gelu_erf(X.astype(np.float64))
+    ref16 = ref.astype(np.float16)
+    # within one fp16 ulp of the correctly rounded fp64 value
+    ulp = np.spacing(np.abs(ref16)).astype(np.float64)
+    assert np.all(np.abs(Y.astype(np.float64) - ref16.astype(np.float64)) <= ulp + 1e-12)
