@@ -20,16 +20,42 @@
 // Wq [N, K]). v_mfma_i32_32x32x32_i8 takes a 32 x 32-byte slice of each: the
 // "A" operand is a 32-row slice of Wq (output features), the "B" operand a
 // 32-row slice of Xq (tokens). A lane's 16 accumulators then hold 4 runs of 4
-// consecutive output features of one token, so the fp16 result leaves as
-// 8-byte stores along a row of Y. A and B fragments use the same lane -> k
-// assignment, so the sum over k is the same whatever order the instruction
-// uses inside its 32-byte slice (integer sums are exact).
+// consecutive output features of one token. A and B fragments use the same
+// lane -> k assignment, so the sum over k is the same whatever order the
+// instruction uses inside its 32-byte slice (integer sums are exact).
 //
-// Block = 4 wavefronts in a 2 x 2 grid over a BN x BM (features x tokens)
-// tile; K advances in 128-byte stages, double-buffered in LDS. Each LDS row
-// is 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at
-// position c ^ (r & 7), so the 16-byte fragment reads of consecutive rows
-// fall on different banks.
+// Block = 4 wavefronts (one per SIMD) in a 2 x 2 grid over a BN x BM
+// (features x tokens) tile; each wave owns a (BN/2) x (BM/2) sub-tile (4 x 4
+// MFMA tiles for 256 x 256), so each 16-byte LDS fragment read feeds 4 MFMAs.
+// K advances in BK-byte stages through a STAGES-deep ring of LDS buffers
+// filled by direct-to-LDS buffer loads (no register staging); the range check
+// of the buffer descriptors zero-fills rows past M / N and, through an
+// out-of-range offset, chunks past K (and whole stages past the end of K).
+//
+// Main loop, step k: wait until stage k+1 has landed, workgroup barrier (stage
+// k+1 visible to every wave; every wave is done reading stage k, whose buffer
+// now takes stage k+STAGES), issue the loads of stage k+STAGES, then the
+// fragment reads of stage k+1 into one register set interleaved with the
+// MFMAs of stage k from the other set, so LDS traffic is spread over the MFMA
+// phase instead of bursting after each barrier.
+//
+// LDS layout of one stage: rows of BK = 64 bytes (Wq rows first, then Xq
+// rows); 16-byte chunk c of row r sits at position c ^ f(r),
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3, so fragment reads of 8 (or 16)
+// consecutive rows at one logical chunk hit distinct 16-byte bank groups of a
+// 128-byte (or 256-byte) bank window.
+//
+// Epilogue: per-tile dequantization with the row / column factors staged in
+// LDS; the fp16 outlier product (at most 16 outlier columns: fragments
+// fetched at kernel start; more: fetched per 16-column step) runs on
+// v_mfma_f32_32x32x16_f16 onto the dequantized tile; the fp16 result goes
+// through a per-wave LDS transpose so that Y leaves as full 128-byte row
+// segments.
+//
+// Tile order: blocks are dealt to the 8 XCDs round-robin by block id; the id
+// is remapped so each XCD owns a contiguous range of tiles, rastered in groups
+// of 8 token-tiles per weight-tile column, so blocks running together on one
+// XCD share their Wq and Xq panels in that XCD's L2.
 
 #include "device_common.h"
 #include "launchers.h"
@@ -38,70 +64,207 @@ namespace i8mm {
 
 namespace {
 
-constexpr int kBK = 128;  // bytes of K per pipeline stage
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN>
+constexpr int kThreads = 256;
+
+template <int BM_, int BN_, int BK_, int STAGES_>
 struct GemmCfg {
-  static constexpr int WM = BM / 2;              // tokens per wave
-  static constexpr int WN = BN / 2;              // features per wave
-  static constexpr int TM = WM / 32;             // MFMA tiles per wave, token dim
-  static constexpr int TN = WN / 32;             // MFMA tiles per wave, feature dim
-  static constexpr int ROWS = BM + BN;           // LDS rows per stage (W rows first)
-  static constexpr int CHUNKS = ROWS * (kBK / 16) / 256;  // 16-byte loads per thread
-  static constexpr int STAGE_BYTES = ROWS * kBK;
-  static_assert(TM >= 1 && TN >= 1, "tile too small");
-  static_assert(ROWS * (kBK / 16) % 256 == 0, "loads must divide evenly");
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WM = BM / 2;                 // tokens per wave
+  static constexpr int WN = BN / 2;                 // features per wave
+  static constexpr int TM = WM / 32;                // MFMA tiles per wave, token dim
+  static constexpr int TN = WN / 32;                // MFMA tiles per wave, feature dim
+  static constexpr int KS = BK / 32;                // MFMA k-steps per stage
+  static constexpr int CPR = BK / 16;               // 16-byte chunks per LDS row
+  static constexpr int ROWS = BM + BN;              // LDS rows per stage
+  static constexpr int STAGE_BYTES = ROWS * BK;
+  static constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide load fills
+  static constexpr int LOADS = ROWS / ROWS_PER_LOAD / 4;  // loads per wave per stage
+  static constexpr int NREADS = KS * (TN + TM);     // fragment reads per stage
+  static constexpr int NMFMA = KS * TN * TM;        // MFMAs per stage
+  // LDS: [scales: sx/127 (BM), sw/127 (BN), bias (BN) floats]
+  //      [outlier tiles: Wo (BN x 16) and Xo (BM x 16) fp16][STAGES stages]
+  static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
+  static constexpr int OUTL0 = SCALE_BYTES;
+  static constexpr int OUTL_BYTES = (BN + BM) * 16 * 2;
+  static constexpr int STAGE0 = (OUTL0 + OUTL_BYTES + 1023) / 1024 * 1024;
+  static constexpr int LDS_BYTES = STAGE0 + STAGES * STAGE_BYTES;
+  // epilogue staging: per wave WM token rows x (WN/2) features fp16, padded
+  static constexpr int OUT_HALF = WN / 2;
+  static constexpr int OUT_ROW = OUT_HALF * 2 + 16;
+  static constexpr int OUT_WAVE = WM * OUT_ROW;
+  static_assert(CPR == 4, "swizzle is written for 4 chunks per row");
+  static_assert(BN % (4 * ROWS_PER_LOAD) == 0 && BM % (4 * ROWS_PER_LOAD) == 0, "split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(4 * OUT_WAVE <= STAGES * STAGE_BYTES, "staging");
+  static_assert(NMFMA % LOADS == 0 && NREADS % LOADS == 0, "interleave");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BM, int BN>
+// Buffer descriptor over [base, base + bytes); reads past `bytes` return 0.
+// The fields go through readfirstlane so the descriptor lives in SGPRs (the
+// callers pass wave-uniform values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS: wait for this wave's LDS operations (an explicit
+// lgkmcnt(0) the compiler accounts for), barrier, then an acquire fence on LDS
+// so later LDS accesses stay after it. A release fence is not used: it would
+// also wait for every in-flight LDS-DMA load, which the explicit vmcnt waits
+// already order.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Token tile / feature tile of this block: XCD-contiguous id, then grouped
+// raster (GROUP token-tiles per feature-tile column).
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int XCDS = 8, GROUP = 8;
+  const int T = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int per = T / XCDS, rem = T % XCDS;
+  const int xcd = b % XCDS, slot = b / XCDS;
+  const int t = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int span = GROUP * tiles_n;
+  const int g = t / span;
+  const int first_m = g * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int in = t - g * span;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+// WITH_C: also write the raw int32 accumulators (parity mode); a separate
+// instantiation so the fp16 path carries none of that code.
+template <class Cfg, bool WITH_C>
 __global__ __launch_bounds__(256) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
-  using Cfg = GemmCfg<BM, BN>;
-  constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN;
-  __shared__ __attribute__((aligned(16))) int8_t lds[2 * Cfg::STAGE_BYTES];
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, STAGES = Cfg::STAGES;
+  constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN, KS = Cfg::KS;
+  constexpr int LOADS = Cfg::LOADS, RPL = Cfg::ROWS_PER_LOAD;
+  __shared__ __attribute__((aligned(1024))) int8_t lds[Cfg::LDS_BYTES];
+  float* s_ax = reinterpret_cast<float*>(lds);          // sx[m] / 127
+  float* s_fw = s_ax + BM;                               // sw[n] / 127
+  float* s_bias = s_fw + BN;                             // bias[n]
+  int8_t* stages = lds + Cfg::STAGE0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int wn = wave & 1, wm = wave >> 1;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  // ---- global -> register staging of one K stage
-  uint4 stage[Cfg::CHUNKS];
-  auto gload = [&](int k0) {
+  int tile_m, tile_n;
+  tile_of_block((M + BM - 1) / BM, (N + BN - 1) / BN, tile_m, tile_n);
+  const int64_t m0 = (int64_t)tile_m * BM;
+  const int64_t n0 = (int64_t)tile_n * BN;
+
+  // ---- outlier columns, 16 at a time: the recovered fp16 weight columns of
+  // this block's BN features and the gathered fp16 activations of its BM
+  // tokens are staged in LDS. Chunk 0 is fetched before the stage loads are
+  // issued and written to LDS after them, so its latency overlaps the
+  // pipeline prologue; further chunks (more than 16 outlier columns) are
+  // staged in the epilogue.
+  const int n_o = (Xo && cols && n_out && Y) ? *n_out : 0;
+  const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
+  uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
+  uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
+  static_assert(BN == kThreads && BM == kThreads, "one row of each outlier tile per thread");
+  int wq_g[16];
+  float sw_mine = 0.0f;
+  uint4 xo_mine[2];
+  auto fetch_outliers = [&](int t0) {
+    const int64_t f = n0 + tid;
+    sw_mine = f < N ? sw[f] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < Cfg::CHUNKS; ++i) {
-      const int idx = tid + i * 256;
-      const int r = idx >> 3, c = idx & 7;
-      const int kk = k0 + c * 16;
-      const int8_t* src;
-      bool ok;
-      if (r < BN) {
-        const int64_t g = n0 + r;
-        ok = g < N && kk < K;
-        src = Wq + g * K + kk;
-      } else {
-        const int64_t g = m0 + (r - BN);
-        ok = g < M && kk < K;
-        src = Xq + g * K + kk;
-      }
-      stage[i] = ok ? ld16(src) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < 16; ++t)
+      wq_g[t] = (f < N && t0 + t < n_o) ? (int)Wq[f * K + cols[t0 + t]] : 0;
+    const int64_t tok = m0 + tid;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      xo_mine[i] = tok < M ? ld16(Xo + tok * ldo + t0 + i * 8) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_outliers = [&]() {
+    uint32_t wpk[8];
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+      const uint32_t lo = f2h(((float)wq_g[t] * sw_mine) / 127.0f);
+      const uint32_t hi = f2h(((float)wq_g[t + 1] * sw_mine) / 127.0f);
+      wpk[t / 2] = lo | (hi << 16);
+    }
+    st16(s_wo + tid * 16, make_uint4(wpk[0], wpk[1], wpk[2], wpk[3]));
+    st16(s_wo + tid * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
+    st16(s_xo + tid * 16, xo_mine[0]);
+    st16(s_xo + tid * 16 + 8, xo_mine[1]);
+  };
+  if (n_o > 0) fetch_outliers(0);
+
+  // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
+  // Wave-wide load j of wave w fills LDS rows R0 .. R0+RPL-1 of the stage,
+  // lane l -> row R0 + l/4, physical chunk l%4, logical chunk (l%4)^f(row).
+  const bool loads_w = wave < 2;
+  const int op_rows_valid =
+      loads_w ? (int)min<int64_t>(BN, N - n0) : (int)min<int64_t>(BM, M - m0);
+  const int8_t* op_base = loads_w ? Wq + n0 * K : Xq + m0 * K;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(op_base, (uint32_t)op_rows_valid * (uint32_t)K);
+  const int row_first = (loads_w ? 0 : BN) + (wave & 1) * (LOADS * RPL);
+  // Lane offsets: load j covers rows row_first + 16j + lane/4; the swizzle
+  // key of those rows depends on j only through its parity.
+  int voff[2], lchunk16[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = row_first + p * RPL + (lane >> 2);
+    const int c = (lane & 3) ^ swz_key(r);
+    voff[p] = (r - (loads_w ? 0 : BN)) * K + c * 16;
+    lchunk16[p] = c * 16;
+  }
+  auto issue_stage = [&](int kt) {
+    const int k0 = kt * BK;
+    int8_t* sbase = stages + (kt % STAGES) * Cfg::STAGE_BYTES + row_first * BK;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int off = (k0 + lchunk16[j & 1] < K) ? voff[j & 1] + (j & ~1) * RPL * K + k0
+                                                  : 0x7ffffff0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, off,
+                                               0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-    int8_t* base = lds + buf * Cfg::STAGE_BYTES;
+
+  // ---- fragment read offsets (bytes inside a stage)
+  int aoff[KS][TN], boff[KS][TM];
 #pragma unroll
-    for (int i = 0; i < Cfg::CHUNKS; ++i) {
-      const int idx = tid + i * 256;
-      const int r = idx >> 3, c = idx & 7;
-      st16(base + swz(r, c), stage[i]);
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks * 2 + lhi;
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const int r = wn * WN + a * 32 + l32;
+      aoff[ks][a] = r * BK + ((c ^ swz_key(r)) << 4);
     }
-  };
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int r = BN + wm * WM + b * 32 + l32;
+      boff[ks][b] = r * BK + ((c ^ swz_key(r)) << 4);
+    }
+  }
 
   v16i32 acc[TN][TM];
 #pragma unroll
@@ -111,58 +274,97 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
-  const int nk = (K + kBK - 1) / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const int8_t* base = lds + buf * Cfg::STAGE_BYTES;
+  v4i32 fa[2][KS][TN], fb[2][KS][TM];
+  auto read_frags = [&](int kt, int set) {
+    const int8_t* base = stages + (kt % STAGES) * Cfg::STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      const int chunk = ks * 2 + lhi;
-      v4i32 fa[TN], fb[TM];
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int a = 0; a < TN; ++a)
-        fa[a] = *reinterpret_cast<const v4i32*>(base + swz(wn * WN + a * 32 + l32, chunk));
+        fa[set][ks][a] = *reinterpret_cast<const v4i32*>(base + aoff[ks][a]);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        fb[b] = *reinterpret_cast<const v4i32*>(base + swz(BN + wm * WM + b * 32 + l32, chunk));
+        fb[set][ks][b] = *reinterpret_cast<const v4i32*>(base + boff[ks][b]);
+    }
+  };
+  auto mfma_stage = [&](int set) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
         for (int b = 0; b < TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b],
+                                                            acc[a][b], 0, 0, 0);
+  };
+  auto step = [&](int k, int set) {
+    wait_vmcnt<(STAGES - 2) * LOADS>();
+    lds_barrier();
+    issue_stage(k + STAGES);
+    read_frags(k + 1, set ^ 1);
+    mfma_stage(set);
+    // Spread the stage loads and the fragment reads over the MFMAs: LOADS
+    // groups of (1 load, NREADS/LOADS reads, NMFMA/LOADS MFMAs).
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, Cfg::NREADS / LOADS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, Cfg::NMFMA / LOADS, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue_stage(s);
+  // Row / column factors into LDS (read by the epilogue after barriers);
+  // issued after the stage loads so the two latencies overlap.
+  if (Y) {
+    for (int i = tid; i < BM; i += kThreads) {
+      const int64_t m = m0 + i;
+      s_ax[i] = m < M ? sx[m] / 127.0f : 0.0f;
+    }
+    for (int i = tid; i < BN; i += kThreads) {
+      const int64_t n = n0 + i;
+      s_fw[i] = n < N ? sw[n] / 127.0f : 0.0f;
+      s_bias[i] = (bias && n < N) ? h2f(bias[n]) : 0.0f;
+    }
   }
+
+  if (n_o > 0) store_outliers();
+  wait_vmcnt<(STAGES - 1) * LOADS>();
+  lds_barrier();
+  read_frags(0, 0);
+  int k = 0;
+  for (; k + 1 < nk; k += 2) {
+    step(k, 0);
+    step(k + 1, 1);
+  }
+  if (k < nk) step(k, 0);
+  wait_vmcnt<0>();
 
   // ---- epilogue
   // Lane (l32, lhi), accumulator r of tile (a, b):
   //   token   = m0 + wm*WM + b*32 + l32
   //   feature = n0 + wn*WN + a*32 + 8*(r/4) + 4*lhi + (r%4)
-  const bool n4 = (N & 3) == 0;
-  int64_t tok[TM];
-#pragma unroll
-  for (int b = 0; b < TM; ++b) tok[b] = m0 + wm * WM + b * 32 + l32;
-
-  if (C) {
+  if (WITH_C) {
+    const bool n4 = (N & 3) == 0;
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        if (tok[b] >= M) continue;
+        const int64_t tok = m0 + wm * WM + b * 32 + l32;
+        if (tok >= M) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t f = n0 + wn * WN + a * 32 + 8 * g + 4 * lhi;
-          int32_t* dst = C + tok[b] * N + f;
+          int32_t* dst = C + tok * N + f;
           if (n4 && f + 3 < N) {
             *reinterpret_cast<int4*>(dst) =
                 make_int4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
                           acc[a][b][4 * g + 3]);
           } else {
+#pragma unroll
             for (int e = 0; e < 4; ++e)
               if (f + e < N) dst[e] = acc[a][b][4 * g + e];
           }
@@ -171,105 +373,125 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   }
   if (!Y) return;
 
-  float ax[TM];
-#pragma unroll
-  for (int b = 0; b < TM; ++b) ax[b] = tok[b] < M ? sx[tok[b]] / 127.0f : 0.0f;
-
-  v16f32 yf[TN][TM];
+  // Dequantize in place: y = C * (sx/127) * (sw/127), all tiles, in fp32.
+  v16f32 yv[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     float fw[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t f = n0 + wn * WN + a * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-      fw[r] = f < N ? sw[f] / 127.0f : 0.0f;
-    }
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) yf[a][b][r] = (float)acc[a][b][r] * ax[b] * fw[r];
-  }
-
-  // fp16 outlier product on v_mfma_f32_32x32x16_f16, 16 outlier columns per
-  // step; A = recovered fp16 weight columns (32 features), B = gathered fp16
-  // activations (32 tokens), same lane -> t assignment on both sides.
-  const int n_o = (Xo && cols && n_out) ? *n_out : 0;
-  if (n_o > 0) {
-    const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
-    for (int t0 = 0; t0 < n_o; t0 += 16) {
-      v8f16 wa[TN], xb[TM];
-#pragma unroll
-      for (int a = 0; a < TN; ++a) {
-        const int64_t f = n0 + wn * WN + a * 32 + l32;
-        const float swf = f < N ? sw[f] : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = t0 + lhi * 8 + e;
-          float w = 0.0f;
-          if (t < n_o && f < N) {
-            const float q = (float)Wq[f * K + cols[t]];
-            w = (q * swf) / 127.0f;
-          }
-          wa[a][e] = (_Float16)w;
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        if (tok[b] < M) {
-          uint4 raw = ld16(Xo + tok[b] * ldo + t0 + lhi * 8);
-          xb[b] = __builtin_bit_cast(v8f16, raw);
-        } else {
-          xb[b] = v8f16{};
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          yf[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[a], xb[b], yf[a][b], 0, 0, 0);
-    }
-  }
-
-#pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    float bv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t f = n0 + wn * WN + a * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-      bv[r] = (bias && f < N) ? h2f(bias[f]) : 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const float4 f4 =
+          *reinterpret_cast<const float4*>(s_fw + wn * WN + a * 32 + 8 * g + 4 * lhi);
+      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
     }
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
-      if (tok[b] >= M) continue;
+      const float ax = s_ax[wm * WM + b * 32 + l32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yv[a][b][r] = (float)acc[a][b][r] * ax * fw[r];
+    }
+  }
+
+  // fp16 outlier product, 16 outlier columns per chunk, on
+  // v_mfma_f32_32x32x16_f16 onto the dequantized tiles: A = recovered weight
+  // columns (32 features), B = gathered activations (32 tokens), read from the
+  // LDS outlier tiles with the same lane -> t assignment on both sides.
+  for (int t0 = 0; t0 < n_o; t0 += 16) {
+    if (t0 > 0) {
+      fetch_outliers(t0);
+      lds_barrier();            // every wave is done with chunk t0-16
+      store_outliers();
+      lds_barrier();
+    }
+    v8f16 xb[TM];
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+      xb[b] = *reinterpret_cast<const v8f16*>(s_xo + (wm * WM + b * 32 + l32) * 16 + lhi * 8);
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const v8f16 wa =
+          *reinterpret_cast<const v8f16*>(s_wo + (wn * WN + a * 32 + l32) * 16 + lhi * 8);
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        yv[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb[b], yv[a][b], 0, 0, 0);
+    }
+  }
+
+  // + bias, round to fp16, and leave through a per-wave LDS transpose so Y is
+  // written as full row segments. All waves are past their last stage reads:
+  // the stage ring becomes the staging area (per wave: WM token rows x WN/2
+  // features).
+  lds_barrier();
+  int8_t* stage_out = stages + wave * Cfg::OUT_WAVE;
+  constexpr int HALF_TN = TN / 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int aa = 0; aa < HALF_TN; ++aa) {
+      const int a = h * HALF_TN + aa;
+      float bv[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t f = n0 + wn * WN + a * 32 + 8 * g + 4 * lhi;
-        uint16_t h[4];
+        const float4 b4 =
+            *reinterpret_cast<const float4*>(s_bias + wn * WN + a * 32 + 8 * g + 4 * lhi);
+        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = f2h(yf[a][b][4 * g + e] + bv[4 * g + e]);
-        uint16_t* dst = Y + tok[b] * N + f;
-        if (n4 && f + 3 < N) {
-          *reinterpret_cast<uint2*>(dst) =
-              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      for (int b = 0; b < TM; ++b) {
+        const int row = b * 32 + l32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t hh[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hh[e] = f2h(yv[a][b][4 * g + e] + bv[4 * g + e]);
+          const int col = aa * 32 + 8 * g + 4 * lhi;   // feature inside the half
+          *reinterpret_cast<uint2*>(stage_out + row * Cfg::OUT_ROW + col * 2) =
+              make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+      }
+    }
+    // Read back rows of WN/2 features (16-byte chunks) and store them.
+    constexpr int CH_ROW = Cfg::OUT_HALF * 2 / 16;     // 16-byte chunks per row
+    constexpr int ROWS_PER_IT = 64 / CH_ROW;
+    const int64_t fcol0 = n0 + wn * WN + h * Cfg::OUT_HALF;
+    const int ch = lane % CH_ROW;
+    const int64_t f = fcol0 + ch * 8;
+    const bool full = f + 7 < N && (N & 7) == 0;
+#pragma unroll 4
+    for (int it = 0; it < WM / ROWS_PER_IT; ++it) {
+      const int row = it * ROWS_PER_IT + lane / CH_ROW;
+      const int64_t tok = m0 + wm * WM + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_out + row * Cfg::OUT_ROW + ch * 16);
+      if (tok < M) {
+        uint16_t* dst = Y + tok * N + f;
+        if (full) {
+          st16(dst, v);
         } else {
-          for (int e = 0; e < 4; ++e)
-            if (f + e < N) dst[e] = h[e];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (f + e < N) dst[e] = (uint16_t)half_of(v, e);
         }
       }
     }
   }
 }
 
-template <int BM, int BN>
+template <class Cfg>
 hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                          hipStream_t s) {
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL((k_gemm_i8<BM, BN>), grid, dim3(256), 0, s, Xq, Wq, sx, sw, (int)M, (int)N,
-                     (int)K, Xo, cols, n_out, bias, Y, C);
+  const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  if (C)
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, true>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
+  else
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, false>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
   return hipGetLastError();
 }
+
+using CfgLarge = GemmCfg<256, 256, 64, 4>;
 
 }  // namespace
 
@@ -278,7 +500,7 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                        hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  return launch_gemm_t<128, 128>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
+  return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
 }
 
 }  // namespace i8mm
