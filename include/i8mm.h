@@ -131,9 +131,9 @@ I8MM_API int int8_quantize_rowwise(const uint16_t* X, int64_t M, int64_t K,
  *
  *   X          fp16 [M, K], read only.
  *   threshold  host float; column k is an outlier iff some abs(X[i,k]) >=
- *              threshold (compared in fp32; NaN inputs never flag; a
- *              threshold <= 0 flags every column; +inf flags columns holding
- *              +-inf). NaN threshold -> EINVAL.
+ *              threshold (exact comparison of the fp16 value) or some X[i,k]
+ *              is NaN; a threshold <= 0 flags every column; +inf flags the
+ *              columns holding +-inf or NaN. NaN threshold -> EINVAL.
  *   bitmap     uint32 [ceil(K/32)], written (bit layout as above).
  *   cols       int32 [K] capacity, written: the outlier columns ascending in
  *              cols[0 .. n-1].

@@ -173,7 +173,7 @@ int outlier_detect_gather(const uint16_t* X, int64_t M, int64_t K, float thresho
   hipStream_t s = (hipStream_t)stream;
   const int64_t nwords = (K + 31) / 32;
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
-  if (M > 0) I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, threshold, bitmap, s), fn));
+  if (M > 0) I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, i8mm::fp16_threshold_pattern(threshold), bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_cols_from_bitmap(bitmap, K, cols, n_outliers, s), fn));
   if (Xo && M > 0)
     I8MM_TRY(launched(
@@ -241,7 +241,7 @@ int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
   uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
   const int64_t nwords = (K + 31) / 32;
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
-  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, threshold, bitmap, s), fn));
+  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, i8mm::fp16_threshold_pattern(threshold), bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
   I8MM_TRY(launched(
       i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, s), fn));

@@ -10,8 +10,13 @@ namespace i8mm {
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
 
-hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau,
+// tau16: smallest fp16 magnitude bit pattern (sign cleared) whose value is
+// >= the threshold (0 for a threshold <= 0, 0x7c00 above the largest finite
+// fp16); see fp16_threshold_pattern.
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, uint32_t tau16,
                                 uint32_t* bitmap, hipStream_t s);
+
+uint32_t fp16_threshold_pattern(float threshold);
 
 hipError_t launch_cols_from_bitmap(const uint32_t* bitmap, int64_t K, int32_t* cols,
                                    int32_t* n_out, hipStream_t s);

@@ -14,6 +14,8 @@
 // Every kernel reads its rows as 16-byte chunks (8 fp16), one chunk per lane,
 // so a wavefront touches 1 KiB of contiguous memory per load.
 
+#include <cmath>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -28,23 +30,19 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t val
   if (i < count) p[i] = value;
 }
 
-// 8 flags, bit e set when abs(element e) >= tau. [HF-blog] "Inside the MatMul"
-// (magnitude 6 or greater) and [Summary] "The full picture" step 1. The fp16
-// value is widened exactly and compared in fp32; NaN never compares true.
-__device__ __forceinline__ uint32_t threshold_flags8(const uint4& v, float tau) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m |= (fabsf(h2f(half_of(v, e))) >= tau ? 1u : 0u) << e;
-  return m;
-}
-
 // Column OR-reduce. Block = 4 waves over one 512-column group; lane owns an
 // 8-column chunk; wave w scans rows r0+w, r0+w+4, ... of the block's row
-// range. Flag bits are merged into the (pre-zeroed) bitmap with atomicOr,
-// which is issued only for chunks that hold an outlier; OR is order-free, so
-// the result does not depend on scheduling.
+// range, keeping the per-column maximum of the fp16 magnitude bit patterns
+// (sign cleared) with packed 16-bit max. For non-NaN values that order is
+// the order of magnitudes, so column k holds some abs(x) >= tau exactly when
+// its maximum pattern is >= tau16, the smallest fp16 pattern whose value is
+// >= tau ([HF-blog] "Inside the MatMul": magnitude 6 or greater; [Summary]
+// "The full picture" step 1). NaN patterns exceed every threshold pattern, so
+// a column holding NaN is flagged too and NaN never enters the int8 path.
+// Flag bits are merged into the (pre-zeroed) bitmap with atomicOr, issued
+// only for chunks that hold an outlier; OR is order-free.
 __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restrict__ X, int64_t M,
-                                                       int64_t K, float tau, int rows_per_block,
+                                                       int64_t K, uint32_t tau16, int rows_per_block,
                                                        uint32_t* __restrict__ bitmap) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -53,17 +51,31 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(M, r0 + (int64_t)rows_per_block);
   const uint16_t* base = X + col0;
-  uint32_t mask = 0;
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mx[4] = {u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}};
+  auto fold = [&](const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u16x2 a = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
+      mx[i] = __builtin_elementwise_max(mx[i], a);
+    }
+  };
   int64_t r = r0 + wave;
   for (; r + 12 < r1; r += 16) {
-    uint4 v0 = ld16(base + r * K);
-    uint4 v1 = ld16(base + (r + 4) * K);
-    uint4 v2 = ld16(base + (r + 8) * K);
-    uint4 v3 = ld16(base + (r + 12) * K);
-    mask |= threshold_flags8(v0, tau) | threshold_flags8(v1, tau) | threshold_flags8(v2, tau) |
-            threshold_flags8(v3, tau);
+    const uint4 v0 = ld16(base + r * K);
+    const uint4 v1 = ld16(base + (r + 4) * K);
+    const uint4 v2 = ld16(base + (r + 8) * K);
+    const uint4 v3 = ld16(base + (r + 12) * K);
+    fold(v0); fold(v1); fold(v2); fold(v3);
   }
-  for (; r < r1; r += 4) mask |= threshold_flags8(ld16(base + r * K), tau);
+  for (; r < r1; r += 4) fold(ld16(base + r * K));
+  uint32_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mask |= ((uint32_t)mx[i][0] >= tau16 ? 1u : 0u) << (2 * i);
+    mask |= ((uint32_t)mx[i][1] >= tau16 ? 1u : 0u) << (2 * i + 1);
+  }
   if (mask) atomicOr(&bitmap[col0 >> 5], mask << (col0 & 31));
 }
 
@@ -125,8 +137,12 @@ __global__ __launch_bounds__(256) void k_cols_from_bitmap(const uint32_t* __rest
   write_cols(sbm, spre, nwords, n, cols, n_out);
 }
 
-// One block per row. CPT = 16-byte chunks per thread kept in registers
-// (K <= CPT * 8 * 256); CPT == 0 streams the row twice (any K).
+// Row pass. Block = 4 wavefronts; each wavefront owns whole rows (rows
+// row0 + wave, row0 + wave + 4, ... of the block's range), so the per-row
+// absmax is a wavefront reduction and the row loop has no block barrier. The
+// outlier bitmap and its popcount prefix are built once per block in LDS.
+// CPT = 16-byte chunks per lane kept in registers (K <= CPT * 8 * 64); CPT ==
+// 0 streams the row twice (any K).
 //
 // Quantization ([HF-blog] "Introduction to model quantization", worked
 // absmax example; "Inside the MatMul": rows of the hidden states, columns of
@@ -142,20 +158,36 @@ __global__ __launch_bounds__(256) void k_cols_from_bitmap(const uint32_t* __rest
 // magnitudes, and the maximum is exact.
 template <int CPT>
 __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, int64_t M,
-                                              int64_t K, const uint32_t* __restrict__ bitmap,
+                                              int64_t K, int rows_per_block,
+                                              const uint32_t* __restrict__ bitmap,
                                               int8_t* __restrict__ Xq, float* __restrict__ sx,
                                               uint16_t* __restrict__ Xo, int32_t* __restrict__ cols,
                                               int32_t* __restrict__ n_out) {
   extern __shared__ uint32_t smem[];
   __shared__ int sred[kRowThreads / kWave];
-  __shared__ uint32_t smax[kRowThreads / kWave];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwords = (int)((K + 31) / 32);
   const int64_t nchunks = K / 8;
   uint32_t* sbm = smem;
   uint32_t* spre = smem + nwords;
-  const uint16_t* xr = X + row * K;
+
+  const int64_t row_lo = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t row_hi = min(M, row_lo + rows_per_block);
+  // The first row's loads are issued before the bitmap is staged, so the two
+  // global round trips overlap; later rows are prefetched one row ahead.
+  uint4 v[CPT > 0 ? CPT : 1];
+  auto load_row = [&](int64_t row) {
+    if constexpr (CPT > 0) {
+      const uint16_t* xr = X + row * K;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int64_t c = lane + (int64_t)j * kWave;
+        v[j] = (row < row_hi && c < nchunks) ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_row(row_lo + wave);
 
   int n = 0;
   if (bitmap) {
@@ -163,94 +195,122 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
     __syncthreads();
     if (Xo || cols || n_out) n = bitmap_prefix(sbm, spre, nwords, sred);
   }
+  if (blockIdx.x == 0) {
+    if (bitmap) write_cols(sbm, spre, nwords, n, cols, n_out);
+    else if (n_out && tid == 0) *n_out = 0;
+  }
   auto outl8 = [&](int64_t c) -> uint32_t {
     if (!bitmap) return 0u;
-    int64_t k = c * 8;
+    const int64_t k = c * 8;
     return (sbm[k >> 5] >> (k & 31)) & 0xffu;
   };
+  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
 
-  // ---- pass 1: absmax of the normal entries
-  uint4 v[CPT > 0 ? CPT : 1];
-  uint32_t mx = 0;
-  if constexpr (CPT > 0) {
+  // Outlier elements of a chunk: gather them to Xo (rare path), then zero
+  // them in the register copy, so the absmax and the codes below need no
+  // per-element test (a zero element has magnitude 0 and code 0).
+  auto strip = [&](int64_t row, int64_t c, uint4& t) {
+    const uint32_t om = outl8(c);
+    if (om) {
+      if (Xo) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      int64_t c = tid + (int64_t)j * kRowThreads;
-      v[j] = c < nchunks ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      int64_t c = tid + (int64_t)j * kRowThreads;
-      uint32_t om = c < nchunks ? outl8(c) : 0xffu;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t m = (om >> e) & 1u ? 0u : (half_of(v[j], e) & 0x7fffu);
-        mx = mx > m ? mx : m;
-      }
-    }
-  } else {
-    for (int64_t c = tid; c < nchunks; c += kRowThreads) {
-      uint4 t = ld16(xr + c * 8);
-      uint32_t om = outl8(c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t m = (om >> e) & 1u ? 0u : (half_of(t, e) & 0x7fffu);
-        mx = mx > m ? mx : m;
-      }
-    }
-  }
-  mx = wave_max_u32(mx);
-  if (lane == 0) smax[wave] = mx;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kRowThreads / kWave; ++i) mx = mx > smax[i] ? mx : smax[i];
-
-  const float a = h2f(mx);
-  const float s = a != 0.0f ? 127.0f / a : 0.0f;
-
-  // ---- pass 2: codes, stores, gather
-  auto emit = [&](int64_t c, const uint4& t) {
-    uint32_t om = outl8(c);
-    if (Xq) {
-      uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float q = __builtin_rintf(h2f(half_of(t, e)) * s);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        int qi = (om >> e) & 1u ? 0 : (int)q;
-        packed[e >> 2] |= ((uint32_t)qi & 0xffu) << ((e & 3) * 8);
-      }
-      *reinterpret_cast<uint2*>(Xq + row * K + c * 8) = make_uint2(packed[0], packed[1]);
-    }
-    if (Xo && om) {
-      const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((om >> e) & 1u) {
-          int64_t k = c * 8 + e;
-          uint32_t w = sbm[k >> 5];
-          int pos = (int)spre[k >> 5] + __popc(w & ((1u << (k & 31)) - 1u));
-          Xo[row * ld + pos] = (uint16_t)half_of(t, e);
+        for (int e = 0; e < 8; ++e) {
+          if ((om >> e) & 1u) {
+            const int64_t k = c * 8 + e;
+            const uint32_t w = sbm[k >> 5];
+            const int pos = (int)spre[k >> 5] + __popc(w & ((1u << (k & 31)) - 1u));
+            Xo[row * ld + pos] = (uint16_t)half_of(t, e);
+          }
         }
       }
+      uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t keep = ((om >> (2 * i)) & 1u ? 0u : 0xffffu) |
+                              ((om >> (2 * i + 1)) & 1u ? 0u : 0xffff0000u);
+        w[i] &= keep;
+      }
+      t = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
-  if constexpr (CPT > 0) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  auto absmax_fold = [&](u16x2 m, const uint4& t) -> u16x2 {
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      int64_t c = tid + (int64_t)j * kRowThreads;
-      if (c < nchunks) emit(c, v[j]);
+    for (int i = 0; i < 4; ++i)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+    return m;
+  };
+  // Codes of 8 elements: y = fl32(x * s); y + 1.5 * 2^23 rounds to the nearest
+  // integer with ties to even (the addend is even and |y| <= 127 < 2^22), so
+  // the low byte of its bit pattern is the two's complement code rne(y). No
+  // clamp is needed: s = fl32(127 / a) and abs(x) <= a give abs(y) <= 127 up
+  // to one rounding, and rne of that is within [-127, 127].
+  auto codes8 = [&](const uint4& t, float s) -> uint2 {
+    const float magic = 12582912.0f;
+    uint32_t r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = h2f(half_of(t, e)) * s;
+      r[e] = __builtin_bit_cast(uint32_t, y + magic);
     }
-  } else {
-    for (int64_t c = tid; c < nchunks; c += kRowThreads) emit(c, ld16(xr + c * 8));
+    const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
+    return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                      __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+  };
+
+  for (int64_t row = row_lo + wave; row < row_hi; row += kRowThreads / kWave) {
+    const uint16_t* xr = X + row * K;
+    u16x2 m2 = u16x2{0, 0};
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int64_t c = lane + (int64_t)j * kWave;
+        if (c < nchunks) strip(row, c, v[j]);
+        m2 = absmax_fold(m2, v[j]);
+      }
+    } else {
+      for (int64_t c = lane; c < nchunks; c += kWave) {
+        uint4 t = ld16(xr + c * 8);
+        strip(row, c, t);
+        m2 = absmax_fold(m2, t);
+      }
+    }
+    uint32_t mx = m2[0] > m2[1] ? m2[0] : m2[1];
+    mx = wave_max_u32(mx);
+    const float a = h2f(mx);
+    const float s = a != 0.0f ? 127.0f / a : 0.0f;
+    if (Xq) {
+      if constexpr (CPT > 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const int64_t c = lane + (int64_t)j * kWave;
+          if (c < nchunks) *reinterpret_cast<uint2*>(Xq + row * K + c * 8) = codes8(v[j], s);
+        }
+      } else {
+        for (int64_t c = lane; c < nchunks; c += kWave) {
+          uint4 t = ld16(xr + c * 8);
+          const uint32_t om = outl8(c);
+          if (om) {
+            uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[i] &= ((om >> (2 * i)) & 1u ? 0u : 0xffffu) |
+                      ((om >> (2 * i + 1)) & 1u ? 0u : 0xffff0000u);
+            t = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          *reinterpret_cast<uint2*>(Xq + row * K + c * 8) = codes8(t, s);
+        }
+      }
+      if (lane == 0) sx[row] = a;
+    }
+    if (Xo)
+      for (int64_t t = n + lane; t < ld; t += kWave) Xo[row * ld + t] = 0;
+    load_row(row + kRowThreads / kWave);
   }
-  if (Xq && tid == 0) sx[row] = a;
-  if (Xo) {
-    const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-    for (int64_t t = n + tid; t < ld; t += kRowThreads) Xo[row * ld + t] = 0;
-  }
-  if (row == 0 && bitmap) write_cols(sbm, spre, nwords, n, cols, n_out);
-  else if (row == 0 && n_out && tid == 0) *n_out = 0;
 }
 
 // Exact-erf GELU in fp32 (activation between the two layers of an MLP block).
@@ -269,13 +329,36 @@ hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t
                          int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                          hipStream_t s) {
   const int nwords = (int)((K + 31) / 32);
-  size_t shm = bitmap ? (size_t)nwords * 2 * sizeof(uint32_t) : 0;
-  hipLaunchKernelGGL(k_rows<CPT>, dim3((unsigned)M), dim3(kRowThreads), shm, s, X, M, K, bitmap,
-                     Xq, sx, Xo, cols, n_out);
+  const size_t shm = bitmap ? (size_t)nwords * 2 * sizeof(uint32_t) : 0;
+  // 4 rows per block (one per wavefront) while that keeps >= 1024 blocks;
+  // more rows per block beyond that amortize the bitmap prefix.
+  int64_t rpb = 4;
+  while (rpb < 64 && (M + rpb * 2 - 1) / (rpb * 2) >= 1024) rpb *= 2;
+  const int64_t blocks = (M + rpb - 1) / rpb;
+  hipLaunchKernelGGL(k_rows<CPT>, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K,
+                     (int)rpb, bitmap, Xq, sx, Xo, cols, n_out);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Value of a non-negative fp16 bit pattern (p <= 0x7c00).
+static double fp16_pattern_value(uint32_t p) {
+  const uint32_t e = (p >> 10) & 0x1f, m = p & 0x3ff;
+  if (e == 0x1f) return HUGE_VAL;
+  if (e == 0) return std::ldexp((double)m, -24);
+  return std::ldexp((double)(1024 + m), (int)e - 25);
+}
+
+uint32_t fp16_threshold_pattern(float threshold) {
+  if (!(threshold > 0.0f)) return 0;          // every magnitude is >= threshold
+  uint32_t lo = 0, hi = 0x7c00;               // value(0x7c00) = inf >= any threshold
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (fp16_pattern_value(mid) >= (double)threshold) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s) {
   if (count <= 0) return hipSuccess;
@@ -285,7 +368,7 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float tau,
+hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, uint32_t tau16,
                                 uint32_t* bitmap, hipStream_t s) {
   if (M <= 0 || K <= 0) return hipSuccess;
   const int64_t col_groups = (K / 8 + 63) / 64;
@@ -294,7 +377,7 @@ hipError_t launch_outlier_flags(const uint16_t* X, int64_t M, int64_t K, float t
   const int rows_per_block = 32;
   const int64_t row_blocks = (M + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(k_outlier_flags, dim3((unsigned)col_groups, (unsigned)row_blocks), dim3(256),
-                     0, s, X, M, K, tau, rows_per_block, bitmap);
+                     0, s, X, M, K, tau16, rows_per_block, bitmap);
   return hipGetLastError();
 }
 
@@ -311,13 +394,14 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* 
                        int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                        hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  const int64_t per_thread = (K / 8 + kRowThreads - 1) / kRowThreads;
-  if (per_thread <= 1) return launch_rows_t<1>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_thread <= 2) return launch_rows_t<2>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_thread <= 4) return launch_rows_t<4>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_thread <= 6) return launch_rows_t<6>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_thread <= 8) return launch_rows_t<8>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_thread <= 16) return launch_rows_t<16>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+  if (per_lane <= 1) return launch_rows_t<1>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 2) return launch_rows_t<2>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 4) return launch_rows_t<4>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 8) return launch_rows_t<8>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 16) return launch_rows_t<16>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 24) return launch_rows_t<24>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  if (per_lane <= 32) return launch_rows_t<32>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
   return launch_rows_t<0>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
 }
 

@@ -32,6 +32,7 @@ W fp16 [N, K] in nn.Linear layout, Y [M, N]):
 
 Readings taken where the pages are open (each is listed in the design doc):
   * threshold test is abs(x) >= tau ("6 or greater" in "Inside the MatMul");
+    a column holding NaN also counts as an outlier column;
   * scale s = fl32(127 / absmax) once per vector, code = rne(fl32(x * s))
     (the worked example of "Introduction to model quantization" divides 127
     by the absmax and multiplies the vector by the result); ties round to
@@ -149,6 +150,9 @@ def detect_outlier_columns(X16, threshold=DEFAULT_THRESHOLD):
     dimension is an outlier when at least one value in it reaches the
     threshold in magnitude. The set is the union over all M rows of the call.
     The comparison is made on exact binary32 images of the fp16 values.
+    Reading (the pages do not cover NaN): a column holding a NaN is an
+    outlier column too, so NaN never enters the int8 path and propagates
+    through the fp16 outlier product instead.
     """
     X = _as_f16(X16).astype(np.float32)
     tau = np.float32(threshold)
@@ -156,7 +160,7 @@ def detect_outlier_columns(X16, threshold=DEFAULT_THRESHOLD):
         raise ValueError("threshold is NaN")
     if X.shape[0] == 0:
         return np.zeros(0, np.int32)
-    flagged = np.any(np.abs(X) >= tau, axis=0)
+    flagged = np.any((np.abs(X) >= tau) | np.isnan(X), axis=0)
     return np.nonzero(flagged)[0].astype(np.int32)
 
 

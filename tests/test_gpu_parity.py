@@ -98,6 +98,26 @@ def test_outlier_threshold_edges(gpu):
     assert _check_detect(gpu, X, -1.0).size == 160
 
 
+def test_outlier_nan_inf_columns(gpu):
+    note("detect nan/inf")
+    rng = np.random.default_rng(6)
+    X = synth.normal_f16(rng, (33, 528), 1.0)
+    X = np.clip(X.astype(np.float32), -5.0, 5.0).astype(np.float16)
+    X[7, 70] = np.float16(np.nan)
+    X[30, 300] = np.float16(np.inf)
+    X[0, 500] = np.float16(-7.0)
+    assert _check_detect(gpu, X, 6.0).tolist() == [70, 300, 500]
+    assert _check_detect(gpu, X, float("inf")).tolist() == [70, 300]
+    assert _check_detect(gpu, X, 1e9).tolist() == [70, 300]
+    # the int8 path stays finite: codes and scales exclude those columns
+    cols = O.detect_outlier_columns(X, 6.0)
+    Xq_ref, sx_ref = O.quantize_activation_rows(X, cols)
+    Xq, sx = _ops(gpu).int8_quantize_rowwise(dev(X), dev(O.outlier_bitmap(cols, 528).view(np.int32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Xq), Xq_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+
+
 def test_outlier_detect_empty_rows(gpu):
     note("detect M=0")
     X = torch.empty((0, 64), dtype=torch.float16, device="cuda")

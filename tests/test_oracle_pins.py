@@ -249,6 +249,17 @@ def test_outlier_detection_brute_force_and_edges():
         O.detect_outlier_columns(X, float("nan"))
 
 
+def test_nan_and_inf_columns_are_outlier_columns():
+    X = np.full((3, 48), 0.5, np.float16)
+    X[1, 7] = np.float16(np.nan)
+    X[2, 20] = np.float16(-np.inf)
+    X[0, 30] = 6.0
+    assert O.detect_outlier_columns(X, 6.0).tolist() == [7, 20, 30]
+    assert O.detect_outlier_columns(X, np.inf).tolist() == [7, 20]
+    Xq, sx = O.quantize_activation_rows(X, O.detect_outlier_columns(X, 6.0))
+    assert np.all(np.isfinite(sx)) and np.all(sx == np.float32(0.5))
+
+
 def test_planted_columns_are_found_and_scales_below_threshold():
     d = synth.tiny()
     cols = O.detect_outlier_columns(d["X"], 6.0)
