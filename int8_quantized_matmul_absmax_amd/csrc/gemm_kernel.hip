@@ -47,10 +47,9 @@
 //
 // Epilogue: per-tile dequantization with the row / column factors staged in
 // LDS; the fp16 outlier product (at most 16 outlier columns: fragments
-// fetched at kernel start; more: fetched per 16-column step) runs on
-// v_mfma_f32_32x32x16_f16 onto the dequantized tile; the fp16 result goes
-// through a per-wave LDS transpose so that Y leaves as full 128-byte row
-// segments.
+// staged at kernel start; more: staged per 16-column step) runs on
+// v_mfma_f32_32x32x16_f16 onto the dequantized tile; lane swaps
+// (v_permlane32_swap) turn each tile into 16-byte row stores.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin by block id; the id
 // is remapped so each XCD owns a contiguous range of tiles, rastered in groups
@@ -90,14 +89,9 @@ struct GemmCfg {
   static constexpr int OUTL_BYTES = (BN + BM) * 16 * 2;
   static constexpr int STAGE0 = (OUTL0 + OUTL_BYTES + 1023) / 1024 * 1024;
   static constexpr int LDS_BYTES = STAGE0 + STAGES * STAGE_BYTES;
-  // epilogue staging: per wave WM token rows x (WN/2) features fp16, padded
-  static constexpr int OUT_HALF = WN / 2;
-  static constexpr int OUT_ROW = OUT_HALF * 2 + 16;
-  static constexpr int OUT_WAVE = WM * OUT_ROW;
   static_assert(CPR == 4, "swizzle is written for 4 chunks per row");
   static_assert(BN % (4 * ROWS_PER_LOAD) == 0 && BM % (4 * ROWS_PER_LOAD) == 0, "split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(4 * OUT_WAVE <= STAGES * STAGE_BYTES, "staging");
   static_assert(NMFMA % LOADS == 0 && NREADS % LOADS == 0, "interleave");
 };
 
@@ -196,8 +190,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     const int64_t f = n0 + tid;
     sw_mine = f < N ? sw[f] : 0.0f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      wq_g[t] = (f < N && t0 + t < n_o) ? (int)Wq[f * K + cols[t0 + t]] : 0;
+    for (int t = 0; t < 16; ++t) {
+      // cols[t0 + t] is the same for every lane (a scalar load)
+      const int c = t0 + t < n_o ? __builtin_amdgcn_readfirstlane(cols[t0 + t]) : 0;
+      wq_g[t] = (f < N && t0 + t < n_o) ? (int)Wq[f * K + c] : 0;
+    }
     const int64_t tok = m0 + tid;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -216,8 +213,6 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     st16(s_xo + tid * 16, xo_mine[0]);
     st16(s_xo + tid * 16 + 8, xo_mine[1]);
   };
-  if (n_o > 0) fetch_outliers(0);
-
   // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
   // Wave-wide load j of wave w fills LDS rows R0 .. R0+RPL-1 of the stage,
   // lane l -> row R0 + l/4, physical chunk l%4, logical chunk (l%4)^f(row).
@@ -315,32 +310,38 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   };
 
   const int nk = (K + BK - 1) / BK;
+  // Prologue, one memory round trip deep: the row / column factors are read
+  // into registers, the first STAGES stages are issued, then the gathers of
+  // the first outlier chunk; the factors go to LDS as soon as they arrive
+  // (they are older than the stage loads), the gathered outlier columns after
+  // the first main-loop step, so their latency overlaps it.
+  float ax_mine = 0.0f, fw_mine = 0.0f, b_mine = 0.0f;
+  if (Y) {
+    static_assert(BM == kThreads && BN == kThreads, "one factor of each kind per thread");
+    const int64_t m = m0 + tid, n = n0 + tid;
+    ax_mine = m < M ? sx[m] : 0.0f;
+    fw_mine = n < N ? sw[n] : 0.0f;
+    b_mine = (bias && n < N) ? h2f(bias[n]) : 0.0f;
+  }
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_stage(s);
-  // Row / column factors into LDS (read by the epilogue after barriers);
-  // issued after the stage loads so the two latencies overlap.
+  if (n_o > 0) fetch_outliers(0);
   if (Y) {
-    for (int i = tid; i < BM; i += kThreads) {
-      const int64_t m = m0 + i;
-      s_ax[i] = m < M ? sx[m] / 127.0f : 0.0f;
-    }
-    for (int i = tid; i < BN; i += kThreads) {
-      const int64_t n = n0 + i;
-      s_fw[i] = n < N ? sw[n] / 127.0f : 0.0f;
-      s_bias[i] = (bias && n < N) ? h2f(bias[n]) : 0.0f;
-    }
+    s_ax[tid] = ax_mine / 127.0f;
+    s_fw[tid] = fw_mine / 127.0f;
+    s_bias[tid] = b_mine;
   }
-
-  if (n_o > 0) store_outliers();
   wait_vmcnt<(STAGES - 1) * LOADS>();
   lds_barrier();
   read_frags(0, 0);
-  int k = 0;
+  step(0, 0);
+  if (n_o > 0) store_outliers();   // read by the epilogue, after later barriers
+  int k = 1;
   for (; k + 1 < nk; k += 2) {
-    step(k, 0);
-    step(k + 1, 1);
+    step(k, 1);
+    step(k + 1, 0);
   }
-  if (k < nk) step(k, 0);
+  if (k < nk) step(k, 1);
   wait_vmcnt<0>();
 
   // ---- epilogue
@@ -373,98 +374,28 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   }
   if (!Y) return;
 
-  // Dequantize in place: y = C * (sx/127) * (sw/127), all tiles, in fp32.
-  v16f32 yv[TN][TM];
+  // ---- fp16 output
+  // Tile (a, b) leaves as 16-byte stores: after packing to fp16, lanes l and
+  // l+32 hold features 8g + 0..3 and 8g + 4..7 of group g; v_permlane32_swap
+  // on groups (g, g+1) gives lane l all 8 features of group g and lane l+32
+  // all 8 of group g+1, so each store instruction writes 32 contiguous bytes
+  // of 32 token rows.
+  const bool n8 = (N & 7) == 0;
+  auto store_tile = [&](int a, int b, const v16f32& y) {
+    const int64_t tok = m0 + wm * WM + b * 32 + l32;
+    uint32_t p[8];
 #pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    float fw[16];
+    for (int i = 0; i < 8; ++i) p[i] = f2h(y[2 * i]) | (f2h(y[2 * i + 1]) << 16);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 f4 =
-          *reinterpret_cast<const float4*>(s_fw + wn * WN + a * 32 + 8 * g + 4 * lhi);
-      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
-    }
-#pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const float ax = s_ax[wm * WM + b * 32 + l32];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) yv[a][b][r] = (float)acc[a][b][r] * ax * fw[r];
-    }
-  }
-
-  // fp16 outlier product, 16 outlier columns per chunk, on
-  // v_mfma_f32_32x32x16_f16 onto the dequantized tiles: A = recovered weight
-  // columns (32 features), B = gathered activations (32 tokens), read from the
-  // LDS outlier tiles with the same lane -> t assignment on both sides.
-  for (int t0 = 0; t0 < n_o; t0 += 16) {
-    if (t0 > 0) {
-      fetch_outliers(t0);
-      lds_barrier();            // every wave is done with chunk t0-16
-      store_outliers();
-      lds_barrier();
-    }
-    v8f16 xb[TM];
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-      xb[b] = *reinterpret_cast<const v8f16*>(s_xo + (wm * WM + b * 32 + l32) * 16 + lhi * 8);
-#pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const v8f16 wa =
-          *reinterpret_cast<const v8f16*>(s_wo + (wn * WN + a * 32 + l32) * 16 + lhi * 8);
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        yv[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb[b], yv[a][b], 0, 0, 0);
-    }
-  }
-
-  // + bias, round to fp16, and leave through a per-wave LDS transpose so Y is
-  // written as full row segments. All waves are past their last stage reads:
-  // the stage ring becomes the staging area (per wave: WM token rows x WN/2
-  // features).
-  lds_barrier();
-  int8_t* stage_out = stages + wave * Cfg::OUT_WAVE;
-  constexpr int HALF_TN = TN / 2;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int aa = 0; aa < HALF_TN; ++aa) {
-      const int a = h * HALF_TN + aa;
-      float bv[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 b4 =
-            *reinterpret_cast<const float4*>(s_bias + wn * WN + a * 32 + 8 * g + 4 * lhi);
-        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
-      }
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        const int row = b * 32 + l32;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t hh[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hh[e] = f2h(yv[a][b][4 * g + e] + bv[4 * g + e]);
-          const int col = aa * 32 + 8 * g + 4 * lhi;   // feature inside the half
-          *reinterpret_cast<uint2*>(stage_out + row * Cfg::OUT_ROW + col * 2) =
-              make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
-        }
-      }
-    }
-    // Read back rows of WN/2 features (16-byte chunks) and store them.
-    constexpr int CH_ROW = Cfg::OUT_HALF * 2 / 16;     // 16-byte chunks per row
-    constexpr int ROWS_PER_IT = 64 / CH_ROW;
-    const int64_t fcol0 = n0 + wn * WN + h * Cfg::OUT_HALF;
-    const int ch = lane % CH_ROW;
-    const int64_t f = fcol0 + ch * 8;
-    const bool full = f + 7 < N && (N & 7) == 0;
-#pragma unroll 4
-    for (int it = 0; it < WM / ROWS_PER_IT; ++it) {
-      const int row = it * ROWS_PER_IT + lane / CH_ROW;
-      const int64_t tok = m0 + wm * WM + row;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage_out + row * Cfg::OUT_ROW + ch * 16);
+    for (int gp = 0; gp < 4; gp += 2) {
+      // p[2gp], p[2gp+1]: group gp; p[2gp+2], p[2gp+3]: group gp+1
+      const auto s0 = __builtin_amdgcn_permlane32_swap(p[2 * gp], p[2 * gp + 2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(p[2 * gp + 1], p[2 * gp + 3], false, false);
+      const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      const int64_t f = n0 + wn * WN + a * 32 + 8 * (gp + lhi);
       if (tok < M) {
         uint16_t* dst = Y + tok * N + f;
-        if (full) {
+        if (n8 && f + 7 < N) {
           st16(dst, v);
         } else {
 #pragma unroll
@@ -472,6 +403,86 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
             if (f + e < N) dst[e] = (uint16_t)half_of(v, e);
         }
       }
+    }
+  };
+  auto load_fw = [&](int a, float* fw, float* bv) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int fl = wn * WN + a * 32 + 8 * g + 4 * lhi;
+      const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
+      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
+      if (bv) {
+        const float4 b4 = *reinterpret_cast<const float4*>(s_bias + fl);
+        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
+      }
+    }
+  };
+  // LDS outlier fragments: 8 fp16 (t = 8*lhi .. 8*lhi+7) of row l32 of a
+  // 32-row slice; same lane -> t assignment on the weight and token side.
+  auto wo_frag = [&](int a) -> v8f16 {
+    return *reinterpret_cast<const v8f16*>(s_wo + (wn * WN + a * 32 + l32) * 16 + lhi * 8);
+  };
+  auto xo_frag = [&](int b) -> v8f16 {
+    return *reinterpret_cast<const v8f16*>(s_xo + (wm * WM + b * 32 + l32) * 16 + lhi * 8);
+  };
+
+  // Fragments of outlier chunks beyond the first (more than 16 outlier
+  // columns), built straight from global memory: the weight columns are
+  // recovered from Wq as fp16(fl32(fl32(q * sw) / 127)), the activations read
+  // from Xo. Slow, but it keeps the per-slice register footprint small.
+  auto wo_frag_g = [&](int a, int t0) -> v8f16 {
+    v8f16 w;
+    const int64_t f = n0 + wn * WN + a * 32 + l32;
+    const float swf = f < N ? sw[f] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + lhi * 8 + e;
+      float v = 0.0f;
+      if (t < n_o && f < N) v = ((float)Wq[f * K + cols[t]] * swf) / 127.0f;
+      w[e] = (_Float16)v;
+    }
+    return w;
+  };
+  auto xo_frag_g = [&](int b, int t0) -> v8f16 {
+    const int64_t tok = m0 + wm * WM + b * 32 + l32;
+    if (tok >= M) return v8f16{};
+    return __builtin_bit_cast(v8f16, ld16(Xo + tok * ldo + t0 + lhi * 8));
+  };
+
+  // One 32-feature slice a at a time, its TM token tiles in VGPRs: dequantize
+  // y = C * (sx/127) * (sw/127), add the fp16 outlier product on
+  // v_mfma_f32_32x32x16_f16 (first 16 columns from the LDS-staged fragments,
+  // further chunks from global memory), add the bias, store.
+#pragma unroll
+  for (int a = 0; a < TN; ++a) {
+    float fw[16], bv[16];
+    load_fw(a, fw, bias ? bv : nullptr);
+    v16f32 y[TM];
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const float ax = s_ax[wm * WM + b * 32 + l32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
+    }
+    if (n_o > 0) {
+      const v8f16 wa = wo_frag(a);
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        y[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xo_frag(b), y[b], 0, 0, 0);
+    }
+    for (int t0 = 16; t0 < n_o; t0 += 16) {
+      const v8f16 wa = wo_frag_g(a, t0);
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        y[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xo_frag_g(b, t0), y[b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      if (bias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[b][r] += bv[r];
+      }
+      store_tile(a, b, y[b]);
     }
   }
 }
