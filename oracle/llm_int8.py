@@ -30,7 +30,7 @@ W fp16 [N, K] in nn.Linear layout, Y [M, N]):
                                                innovation", "The full picture" step 3]
   4. add the two parts                         [Summary "The full picture" step 4]
 
-Readings taken where the pages are open (each is listed in the design doc):
+Readings taken where the pages are open:
   * threshold test is abs(x) >= tau ("6 or greater" in "Inside the MatMul");
     a column holding NaN also counts as an outlier column;
   * scale s = fl32(127 / absmax) once per vector, code = rne(fl32(x * s))

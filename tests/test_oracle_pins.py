@@ -412,3 +412,22 @@ def test_bias_is_added():
     r0 = O.linear_int8_mixed(d["X"], Wq, sw)
     r1 = O.linear_int8_mixed(d["X"], Wq, sw, bias=b)
     assert np.allclose(r1["Y"] - r0["Y"], b.astype(np.float64)[None, :], rtol=0, atol=1e-12)
+
+
+def test_gelu_closed_forms():
+    """GELU(x) = x * Phi(x) with Phi the standard normal CDF: textbook table
+    values of Phi, the odd-part identity GELU(x) - GELU(-x) = x, and the tails."""
+    # Phi(1) and Phi(1.96) from standard normal tables (16 digits).
+    assert abs(O.gelu_erf(1.0) - 0.8413447460685429) < 1e-14
+    assert abs(O.gelu_erf(1.96) - 1.96 * 0.9750021048517795) < 1e-14
+    assert O.gelu_erf(0.0) == 0.0
+    x = np.linspace(-9, 9, 181)
+    assert np.allclose(O.gelu_erf(x) - O.gelu_erf(-x), x, rtol=0, atol=1e-13)
+    assert abs(O.gelu_erf(12.0) - 12.0) < 1e-12 and abs(O.gelu_erf(-12.0)) < 1e-12
+
+
+def test_max_abs_rel_error_definition():
+    ref = np.array([[1.0, -4.0], [2.0, 0.0]])
+    test = ref + np.array([[0.0, 0.02], [-0.04, 0.01]])
+    assert abs(O.max_abs_rel_error(test, ref) - 0.01) < 1e-15
+    assert O.max_abs_rel_error(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
