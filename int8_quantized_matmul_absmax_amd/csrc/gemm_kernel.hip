@@ -49,7 +49,8 @@
 // LDS; the fp16 outlier product (at most 16 outlier columns: fragments
 // staged at kernel start; more: staged per 16-column step) runs on
 // v_mfma_f32_32x32x16_f16 onto the dequantized tile; lane swaps
-// (v_permlane32_swap) turn each tile into 16-byte row stores.
+// (v_permlane32_swap) and a pass through LDS turn each pair of 32-feature
+// slices into whole 128-byte row segments of Y per 8 lanes.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin by block id; the id
 // is remapped so each XCD owns a contiguous range of tiles, rastered in groups
@@ -343,6 +344,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   }
   if (k < nk) step(k, 1);
   wait_vmcnt<0>();
+  // every wave is done with the stage buffers before the epilogue reuses them
+  if (Y) lds_barrier();
 
   // ---- epilogue
   // Lane (l32, lhi), accumulator r of tile (a, b):
@@ -375,14 +378,20 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   if (!Y) return;
 
   // ---- fp16 output
-  // Tile (a, b) leaves as 16-byte stores: after packing to fp16, lanes l and
-  // l+32 hold features 8g + 0..3 and 8g + 4..7 of group g; v_permlane32_swap
-  // on groups (g, g+1) gives lane l all 8 features of group g and lane l+32
-  // all 8 of group g+1, so each store instruction writes 32 contiguous bytes
-  // of 32 token rows.
+  // Two 32-feature slices at a time go through this wave's part of the (now
+  // idle) stage buffers: after packing to fp16, lanes l and l+32 hold
+  // features 8g + 0..3 and 8g + 4..7 of group g; v_permlane32_swap on groups
+  // (g, g+1) gives lane l all 8 features of group g and lane l+32 all 8 of
+  // group g+1, written to LDS as 16-byte pieces of [token][64 features] rows.
+  // They are read back row-contiguous, so 8 consecutive lanes store one whole
+  // 128-byte row segment of Y: write misses reach memory as full lines
+  // rather than as 16-byte pieces of 32 different rows.
+  constexpr int OUT_ROW = 64 * 2 + 16;               // bytes per staged row (+ pad)
+  static_assert(4 * WM * OUT_ROW <= STAGES * Cfg::STAGE_BYTES, "output staging fits");
+  static_assert(TN % 2 == 0, "slices are stored in pairs");
+  int8_t* s_out = stages + wave * (WM * OUT_ROW);
   const bool n8 = (N & 7) == 0;
-  auto store_tile = [&](int a, int b, const v16f32& y) {
-    const int64_t tok = m0 + wm * WM + b * 32 + l32;
+  auto stage_tile = [&](int a, int b, const v16f32& y) {
     uint32_t p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = f2h(y[2 * i]) | (f2h(y[2 * i + 1]) << 16);
@@ -391,8 +400,23 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
       // p[2gp], p[2gp+1]: group gp; p[2gp+2], p[2gp+3]: group gp+1
       const auto s0 = __builtin_amdgcn_permlane32_swap(p[2 * gp], p[2 * gp + 2], false, false);
       const auto s1 = __builtin_amdgcn_permlane32_swap(p[2 * gp + 1], p[2 * gp + 3], false, false);
-      const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-      const int64_t f = n0 + wn * WN + a * 32 + 8 * (gp + lhi);
+      const int row = b * 32 + l32;
+      const int col = (a & 1) * 64 + 16 * (gp + lhi);   // byte offset in the row
+      *reinterpret_cast<uint4*>(s_out + row * OUT_ROW + col) =
+          make_uint4(s0[0], s1[0], s0[1], s1[1]);
+    }
+  };
+  auto flush_pair = [&](int a0) {
+    // a0 even: slices a0, a0+1 = features wn*WN + a0*32 + [0, 64)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t f = n0 + wn * WN + a0 * 32 + 8 * (lane & 7);
+#pragma unroll 4
+    for (int it = 0; it < WM / 8; ++it) {
+      const int row = it * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(s_out + row * OUT_ROW + 16 * (lane & 7));
+      const int64_t tok = m0 + wm * WM + row;
       if (tok < M) {
         uint16_t* dst = Y + tok * N + f;
         if (n8 && f + 7 < N) {
@@ -404,6 +428,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   auto load_fw = [&](int a, float* fw, float* bv) {
 #pragma unroll
@@ -482,8 +509,9 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
 #pragma unroll
         for (int r = 0; r < 16; ++r) y[b][r] += bv[r];
       }
-      store_tile(a, b, y[b]);
+      stage_tile(a, b, y[b]);
     }
+    if (a & 1) flush_pair(a - 1);
   }
 }
 
