@@ -233,16 +233,18 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     voff[p] = (r - (loads_w ? 0 : BN)) * K + c * 16;
     lchunk16[p] = c * 16;
   }
-  auto issue_stage = [&](int kt) {
+  // Wave-wide load j of stage kt (LOADS per wave per stage).
+  auto issue_load = [&](int kt, int j) {
     const int k0 = kt * BK;
     int8_t* sbase = stages + (kt % STAGES) * Cfg::STAGE_BYTES + row_first * BK;
+    const int off = (k0 + lchunk16[j & 1] < K) ? voff[j & 1] + (j & ~1) * RPL * K + k0
+                                                : 0x7ffffff0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, off,
+                                             0, 0, 0);
+  };
+  auto issue_stage = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int off = (k0 + lchunk16[j & 1] < K) ? voff[j & 1] + (j & ~1) * RPL * K + k0
-                                                  : 0x7ffffff0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, off,
-                                               0, 0, 0);
-    }
+    for (int j = 0; j < LOADS; ++j) issue_load(kt, j);
   };
 
   // ---- fragment read offsets (bytes inside a stage)
@@ -271,43 +273,52 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
   v4i32 fa[2][KS][TN], fb[2][KS][TM];
+  // Fragment r of a stage, in the order the MFMAs of a step consume them:
+  // per k-step ks, A tile 0, B tiles 0..TM-1, then A tiles 1..TN-1.
+  auto read_one = [&](const int8_t* base, int r, int set) {
+    const int ks = r / (TN + TM), i = r % (TN + TM);
+    if (i == 0)
+      fa[set][ks][0] = *reinterpret_cast<const v4i32*>(base + aoff[ks][0]);
+    else if (i <= TM)
+      fb[set][ks][i - 1] = *reinterpret_cast<const v4i32*>(base + boff[ks][i - 1]);
+    else
+      fa[set][ks][i - TM] = *reinterpret_cast<const v4i32*>(base + aoff[ks][i - TM]);
+  };
   auto read_frags = [&](int kt, int set) {
     const int8_t* base = stages + (kt % STAGES) * Cfg::STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-        fa[set][ks][a] = *reinterpret_cast<const v4i32*>(base + aoff[ks][a]);
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        fb[set][ks][b] = *reinterpret_cast<const v4i32*>(base + boff[ks][b]);
-    }
+    for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, set);
   };
-  auto mfma_stage = [&](int set) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b],
-                                                            acc[a][b], 0, 0, 0);
+  // MFMA m of a step: k-step ks, A tile a, B tile b.
+  auto mfma_one = [&](int m, int set) {
+    const int ks = m / (TN * TM), a = (m / TM) % TN, b = m % TM;
+    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b], acc[a][b],
+                                                      0, 0, 0);
   };
+  // Step k: wait until stage k+1 has landed, barrier (stage k+1 visible to
+  // every wave; every wave is done reading stage k, whose buffer now takes
+  // stage k+STAGES), then LOADS groups in a fixed order, each of one stage
+  // load, a few fragment reads of stage k+1 into the other register set, and
+  // NMFMA/LOADS MFMAs on stage k. The reads fill the first RGROUPS groups so
+  // they have landed by the next barrier's LDS wait; the scheduling barriers
+  // keep the compiler from regrouping them (which would force both register
+  // sets into one and serialize the reads behind the MFMAs).
+  constexpr int RGROUPS = LOADS * 3 / 4;
+  constexpr int MPG = Cfg::NMFMA / LOADS;
   auto step = [&](int k, int set) {
     wait_vmcnt<(STAGES - 2) * LOADS>();
     lds_barrier();
-    issue_stage(k + STAGES);
-    read_frags(k + 1, set ^ 1);
-    mfma_stage(set);
-    // Spread the stage loads and the fragment reads over the MFMAs: LOADS
-    // groups of (1 load, NREADS/LOADS reads, NMFMA/LOADS MFMAs).
+    const int8_t* rbase = stages + ((k + 1) % STAGES) * Cfg::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, Cfg::NREADS / LOADS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, Cfg::NMFMA / LOADS, 0);
+    for (int g = 0; g < LOADS; ++g) {
+      issue_load(k + STAGES, g);
+#pragma unroll
+      for (int r = 0; r < Cfg::NREADS; ++r)
+        if (r * RGROUPS / Cfg::NREADS == g) read_one(rbase, r, set ^ 1);
+#pragma unroll
+      for (int m = g * MPG; m < (g + 1) * MPG; ++m) mfma_one(m, set);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   const int nk = (K + BK - 1) / BK;
