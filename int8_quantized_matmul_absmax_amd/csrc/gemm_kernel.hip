@@ -550,6 +550,7 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                        hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (gemv_applies(M)) return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
   return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
 }
 

@@ -33,6 +33,14 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
                        uint16_t* Y, int32_t* C, hipStream_t s);
 
+// Few-token form of launch_gemm (same arguments and results), used for
+// 1 <= M <= 64.
+bool gemv_applies(int64_t M);
+hipError_t launch_gemv(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
+                       int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
+                       const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
+                       uint16_t* Y, int32_t* C, hipStream_t s);
+
 hipError_t launch_gelu(const uint16_t* X, int64_t count, uint16_t* Y, hipStream_t s);
 
 }  // namespace i8mm

@@ -152,7 +152,8 @@ def test_rowwise_quant_bitexact(gpu, case):
 # ------------------------------------------------------------------ a5: int32 GEMM
 
 @pytest.mark.parametrize("mnk", [(1, 1, 16), (7, 50, 48), (130, 260, 272), (300, 1000, 4112),
-                                 (16, 4096, 4096), (256, 384, 1024)])
+                                 (16, 4096, 4096), (256, 384, 1024), (17, 33, 272),
+                                 (33, 130, 1040), (64, 64, 4096), (65, 40, 528), (63, 17, 8208)])
 def test_int32_accumulators_bitexact(gpu, mnk):
     M, N, K = mnk
     note("int32 gemm %s" % (mnk,))
@@ -278,6 +279,26 @@ def test_linear_edge_cases(gpu, case):
         assert ref["cols"].tolist() == [7, 100]
     if case in ("n17", "n33"):
         assert ref["n"] >= int(case[1:])
+
+
+@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 31, 33, 48, 63, 64, 65, 97])
+def test_linear_token_counts(gpu, M):
+    """Token counts around the 16-token groups of the few-token path and its
+    hand-over to the tiled GEMM, with ragged N and K and 20 outlier columns."""
+    note("linear M=%d" % M)
+    rng = np.random.default_rng(100 + M)
+    X = synth.normal_f16(rng, (M, 1040), 1.0)
+    W = synth.normal_f16(rng, (300, 1040), 0.05)
+    synth.plant_outlier_columns(rng, X, 20, 7.0, 30.0, (0.0, 1.0))
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0)
+    Y, views = _run_linear(gpu, X, Wq, sw, 6.0)
+    _check_intermediates(gpu, views, X, ref)
+    assert y_err(Y, ref["Y"]) <= Y_TOL
+    C = _ops(gpu).int8_mm_dequant(views["Xq"], dev(Wq), views["sx"], dev(sw), want_y=False,
+                                  want_int32=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(C), O.int32_accumulators(ref["Xq"], Wq))
 
 
 def test_linear_is_deterministic(gpu):
