@@ -183,23 +183,25 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
-  static_assert(BN == kThreads && BM == kThreads, "one row of each outlier tile per thread");
+  static_assert(BN <= kThreads && BM <= kThreads, "at most one row of each outlier tile per thread");
   int wq_g[16];
   float sw_mine = 0.0f;
   uint4 xo_mine[2];
   auto fetch_outliers = [&](int t0) {
     const int64_t f = n0 + tid;
-    sw_mine = f < N ? sw[f] : 0.0f;
+    const bool f_ok = tid < BN && f < N;
+    sw_mine = f_ok ? sw[f] : 0.0f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       // cols[t0 + t] is the same for every lane (a scalar load)
       const int c = t0 + t < n_o ? __builtin_amdgcn_readfirstlane(cols[t0 + t]) : 0;
-      wq_g[t] = (f < N && t0 + t < n_o) ? (int)Wq[f * K + c] : 0;
+      wq_g[t] = (f_ok && t0 + t < n_o) ? (int)Wq[f * K + c] : 0;
     }
     const int64_t tok = m0 + tid;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      xo_mine[i] = tok < M ? ld16(Xo + tok * ldo + t0 + i * 8) : make_uint4(0, 0, 0, 0);
+      xo_mine[i] = (tid < BM && tok < M) ? ld16(Xo + tok * ldo + t0 + i * 8)
+                                          : make_uint4(0, 0, 0, 0);
   };
   auto store_outliers = [&]() {
     uint32_t wpk[8];
@@ -209,10 +211,14 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
       const uint32_t hi = f2h(((float)wq_g[t + 1] * sw_mine) / 127.0f);
       wpk[t / 2] = lo | (hi << 16);
     }
-    st16(s_wo + tid * 16, make_uint4(wpk[0], wpk[1], wpk[2], wpk[3]));
-    st16(s_wo + tid * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
-    st16(s_xo + tid * 16, xo_mine[0]);
-    st16(s_xo + tid * 16 + 8, xo_mine[1]);
+    if (tid < BN) {
+      st16(s_wo + tid * 16, make_uint4(wpk[0], wpk[1], wpk[2], wpk[3]));
+      st16(s_wo + tid * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
+    }
+    if (tid < BM) {
+      st16(s_xo + tid * 16, xo_mine[0]);
+      st16(s_xo + tid * 16 + 8, xo_mine[1]);
+    }
   };
   // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
   // Wave-wide load j of wave w fills LDS rows R0 .. R0+RPL-1 of the stage,
@@ -329,19 +335,21 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // the first main-loop step, so their latency overlaps it.
   float ax_mine = 0.0f, fw_mine = 0.0f, b_mine = 0.0f;
   if (Y) {
-    static_assert(BM == kThreads && BN == kThreads, "one factor of each kind per thread");
+    static_assert(BM <= kThreads && BN <= kThreads, "at most one factor of each kind per thread");
     const int64_t m = m0 + tid, n = n0 + tid;
-    ax_mine = m < M ? sx[m] : 0.0f;
-    fw_mine = n < N ? sw[n] : 0.0f;
-    b_mine = (bias && n < N) ? h2f(bias[n]) : 0.0f;
+    ax_mine = (tid < BM && m < M) ? sx[m] : 0.0f;
+    fw_mine = (tid < BN && n < N) ? sw[n] : 0.0f;
+    b_mine = (bias && tid < BN && n < N) ? h2f(bias[n]) : 0.0f;
   }
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_stage(s);
   if (n_o > 0) fetch_outliers(0);
   if (Y) {
-    s_ax[tid] = ax_mine / 127.0f;
-    s_fw[tid] = fw_mine / 127.0f;
-    s_bias[tid] = b_mine;
+    if (tid < BM) s_ax[tid] = ax_mine / 127.0f;
+    if (tid < BN) {
+      s_fw[tid] = fw_mine / 127.0f;
+      s_bias[tid] = b_mine;
+    }
   }
   wait_vmcnt<(STAGES - 1) * LOADS>();
   lds_barrier();
@@ -542,6 +550,11 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
 }
 
 using CfgLarge = GemmCfg<256, 256, 64, 4>;
+using CfgSmall = GemmCfg<128, 128, 64, 4>;
+#ifndef I8MM_LARGE_TILE_MIN
+#define I8MM_LARGE_TILE_MIN 256
+#endif
+constexpr int64_t kLargeTileMin = I8MM_LARGE_TILE_MIN;
 
 }  // namespace
 
@@ -551,7 +564,12 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (gemv_applies(M)) return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
-  return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
+  // 256 x 256 tiles when they give every CU at least one; otherwise the
+  // 128 x 128 tiles (four times as many, two blocks per CU).
+  const int64_t tiles_large = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles_large >= kLargeTileMin)
+    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
+  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
 }
 
 }  // namespace i8mm

@@ -153,7 +153,8 @@ def test_rowwise_quant_bitexact(gpu, case):
 
 @pytest.mark.parametrize("mnk", [(1, 1, 16), (7, 50, 48), (130, 260, 272), (300, 1000, 4112),
                                  (16, 4096, 4096), (256, 384, 1024), (17, 33, 272),
-                                 (33, 130, 1040), (64, 64, 4096), (65, 40, 528), (63, 17, 8208)])
+                                 (33, 130, 1040), (64, 64, 4096), (65, 40, 528), (63, 17, 8208),
+                                 (4100, 4100, 272)])
 def test_int32_accumulators_bitexact(gpu, mnk):
     M, N, K = mnk
     note("int32 gemm %s" % (mnk,))
@@ -279,6 +280,22 @@ def test_linear_edge_cases(gpu, case):
         assert ref["cols"].tolist() == [7, 100]
     if case in ("n17", "n33"):
         assert ref["n"] >= int(case[1:])
+
+
+def test_linear_large_tiles_ragged(gpu):
+    """A shape with enough 256 x 256 tiles for the large-tile GEMM, ragged in M
+    and N, with outlier columns and a bias."""
+    note("linear large tiles ragged")
+    rng = np.random.default_rng(41)
+    X = synth.normal_f16(rng, (4100, 528), 1.0)
+    W = synth.normal_f16(rng, (4100, 528), 0.05)
+    synth.plant_outlier_columns(rng, X, 9, 7.0, 30.0, 0.5)
+    bias = synth.normal_f16(rng, (4100,), 0.5)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0, bias)
+    Y, views = _run_linear(gpu, X, Wq, sw, 6.0, bias)
+    _check_intermediates(gpu, views, X, ref)
+    assert y_err(Y, ref["Y"]) <= Y_TOL
 
 
 @pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 31, 33, 48, 63, 64, 65, 97])
