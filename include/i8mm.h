@@ -197,7 +197,10 @@ I8MM_API int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx
  *   workspace  device buffer of at least linear_int8_mixed_workspace_bytes(M,K)
  *              bytes, 256-byte aligned; it receives the intermediates (outlier
  *              bitmap, cols, n, sx, Xq, Xo) at the offsets that
- *              i8mm_workspace_offsets reports.
+ *              i8mm_workspace_offsets reports. Given at least
+ *              linear_int8_mixed_workspace_bytes_many_outliers(M, K, N) bytes,
+ *              the recovered outlier weight columns go after them (see that
+ *              call) and many outlier columns take the fast path.
  *
  * All kernels run in order on `stream` with no host synchronization; the
  * outlier count stays on the device. Errors: EINVAL, EALIGN, EWORKSPACE,
@@ -211,6 +214,19 @@ I8MM_API int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
 /* Bytes of workspace linear_int8_mixed needs for M tokens and K features
  * (0 if the sizes are invalid). Host-only, pure. */
 I8MM_API size_t linear_int8_mixed_workspace_bytes(int64_t M, int64_t K);
+
+/* Bytes of workspace with which linear_int8_mixed also takes its fast path
+ * for many outlier columns (0 if the sizes are invalid). Host-only, pure.
+ * It is the size above plus a region, starting at
+ * linear_int8_mixed_workspace_bytes(M, K), for the recovered fp16 weight
+ * columns of the outlier columns ([HF-blog] "Usage": CB * SCB / 127 per
+ * output row), Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)),
+ * N rows of I8MM_OUTLIER_LD(n) halfs. With more than 16 outlier columns (and
+ * more than 64 tokens) the layer fills that region and runs the outlier
+ * product as a second main loop of its GEMM over the outlier columns; given
+ * only the smaller workspace it computes the same result with the outlier
+ * product in the GEMM's epilogue, which is slow for many outlier columns. */
+I8MM_API size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64_t K, int64_t N);
 
 /* Byte offsets inside the workspace, host-only and pure. Writes, in order:
  * offsets[0] bitmap (uint32 [ceil(K/32)]), [1] cols (int32 [K]),

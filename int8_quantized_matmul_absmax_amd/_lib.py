@@ -23,6 +23,7 @@ EXPORTS = (
     "int8_mm_dequant",
     "linear_int8_mixed",
     "linear_int8_mixed_workspace_bytes",
+    "linear_int8_mixed_workspace_bytes_many_outliers",
     "i8mm_workspace_offsets",
     "i8mm_gelu_f16",
     "i8mm_last_error",
@@ -55,6 +56,7 @@ def _declare(lib):
         "linear_int8_mixed": ([vp, i64, i64, vp, vp, i64, vp, f32, vp, vp, ctypes.c_size_t, vp],
                               i32),
         "linear_int8_mixed_workspace_bytes": ([i64, i64], ctypes.c_size_t),
+        "linear_int8_mixed_workspace_bytes_many_outliers": ([i64, i64, i64], ctypes.c_size_t),
         "i8mm_workspace_offsets": ([i64, i64, ctypes.POINTER(ctypes.c_int64)], i32),
         "i8mm_gelu_f16": ([vp, i64, vp, vp], i32),
         "i8mm_last_error": ([], ctypes.c_char_p),

@@ -98,6 +98,12 @@ bool layout(int64_t M, int64_t K, int64_t* off) {
   return true;
 }
 
+// Bytes of the optional region after the minimal workspace: the recovered
+// fp16 outlier weight columns, [N, I8MM_OUTLIER_LD(K)] at most.
+int64_t wo_region_bytes(int64_t N, int64_t K) {
+  return round_up(N * I8MM_OUTLIER_LD(K) * 2, kAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +126,12 @@ const char* i8mm_status_string(int status) {
 size_t linear_int8_mixed_workspace_bytes(int64_t M, int64_t K) {
   int64_t off[7];
   return layout(M, K, off) ? (size_t)off[6] : 0;
+}
+
+size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64_t K, int64_t N) {
+  int64_t off[7];
+  if (N < 0 || N > INT32_MAX || !layout(M, K, off)) return 0;
+  return (size_t)(off[6] + wo_region_bytes(N, K));
 }
 
 int i8mm_workspace_offsets(int64_t M, int64_t K, int64_t* offsets) {
@@ -206,7 +218,8 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
   I8MM_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, s), fn));
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr, s),
+      fn));
   return ok();
 }
 
@@ -243,8 +256,15 @@ int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
   I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, i8mm::fp16_threshold_pattern(threshold), bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+  // With room for it, the recovered outlier weight columns are materialized
+  // for the tiled GEMM (the kernel does nothing for 16 or fewer columns).
+  uint16_t* Wo = nullptr;
+  if (!i8mm::gemv_applies(M) && (int64_t)workspace_bytes >= off[6] + wo_region_bytes(N, K)) {
+    Wo = reinterpret_cast<uint16_t*>(ws + off[6]);
+    I8MM_TRY(launched(i8mm::launch_recover_outlier_w(Wq, sw, N, K, cols, n_o, Wo, s), fn));
+  }
   I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, s), fn));
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, Wo, s), fn));
   return ok();
 }
 

@@ -57,6 +57,8 @@
 // of 8 token-tiles per weight-tile column, so blocks running together on one
 // XCD share their Wq and Xq panels in that XCD's L2.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C,
+    const uint16_t* __restrict__ Wo) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN, KS = Cfg::KS;
   constexpr int LOADS = Cfg::LOADS, RPL = Cfg::ROWS_PER_LOAD;
@@ -181,6 +184,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // staged in the epilogue.
   const int n_o = (Xo && cols && n_out && Y) ? *n_out : 0;
   const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
+  // More than 16 outlier columns with the recovered weights materialized (Wo
+  // [N, ldo] fp16): the outlier product runs as a second main-loop segment
+  // over the outlier columns (fp16 MFMA on Wo and Xo through the same stage
+  // pipeline) instead of in the epilogue.
+  const bool seg2 = !WITH_C && Wo != nullptr && n_o > 16;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
   static_assert(BN <= kThreads && BM <= kThreads, "at most one row of each outlier tile per thread");
@@ -227,24 +235,31 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   const int op_rows_valid =
       loads_w ? (int)min<int64_t>(BN, N - n0) : (int)min<int64_t>(BM, M - m0);
   const int8_t* op_base = loads_w ? Wq + n0 * K : Xq + m0 * K;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(op_base, (uint32_t)op_rows_valid * (uint32_t)K);
+  // Operand rows are `rstride` bytes apart and hold `rowbytes` bytes of K
+  // (the int8 codes: K and K; the outlier segment: 2 * ldo and 2 * ldo).
+  __amdgpu_buffer_rsrc_t rsrc = make_rsrc(op_base, (uint32_t)op_rows_valid * (uint32_t)K);
+  int rstride = K, rowbytes = K;
   const int row_first = (loads_w ? 0 : BN) + (wave & 1) * (LOADS * RPL);
   // Lane offsets: load j covers rows row_first + 16j + lane/4; the swizzle
   // key of those rows depends on j only through its parity.
   int voff[2], lchunk16[2];
+  auto set_offsets = [&]() {
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = row_first + p * RPL + (lane >> 2);
-    const int c = (lane & 3) ^ swz_key(r);
-    voff[p] = (r - (loads_w ? 0 : BN)) * K + c * 16;
-    lchunk16[p] = c * 16;
-  }
+    for (int p = 0; p < 2; ++p) {
+      const int r = row_first + p * RPL + (lane >> 2);
+      const int c = (lane & 3) ^ swz_key(r);
+      voff[p] = (r - (loads_w ? 0 : BN)) * rstride + c * 16;
+      lchunk16[p] = c * 16;
+    }
+  };
+  set_offsets();
   // Wave-wide load j of stage kt (LOADS per wave per stage).
   auto issue_load = [&](int kt, int j) {
     const int k0 = kt * BK;
     int8_t* sbase = stages + (kt % STAGES) * Cfg::STAGE_BYTES + row_first * BK;
-    const int off = (k0 + lchunk16[j & 1] < K) ? voff[j & 1] + (j & ~1) * RPL * K + k0
-                                                : 0x7ffffff0;
+    const int off = (k0 + lchunk16[j & 1] < rowbytes)
+                        ? voff[j & 1] + (j & ~1) * RPL * rstride + k0
+                        : 0x7ffffff0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, off,
                                              0, 0, 0);
   };
@@ -295,11 +310,20 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
 #pragma unroll
     for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, set);
   };
-  // MFMA m of a step: k-step ks, A tile a, B tile b.
-  auto mfma_one = [&](int m, int set) {
+  // MFMA m of a step: k-step ks, A tile a, B tile b. The outlier segment
+  // reads the same 16-byte fragments as 8 fp16 values (16 k per MFMA instead
+  // of 32) and keeps its fp32 sums in the same accumulator registers.
+  auto mfma_one = [&](int m, int set, auto f16) {
     const int ks = m / (TN * TM), a = (m / TM) % TN, b = m % TM;
-    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b], acc[a][b],
-                                                      0, 0, 0);
+    if constexpr (decltype(f16)::value) {
+      const v16f32 r = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          __builtin_bit_cast(v8f16, fa[set][ks][a]), __builtin_bit_cast(v8f16, fb[set][ks][b]),
+          __builtin_bit_cast(v16f32, acc[a][b]), 0, 0, 0);
+      acc[a][b] = __builtin_bit_cast(v16i32, r);
+    } else {
+      acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b],
+                                                        acc[a][b], 0, 0, 0);
+    }
   };
   // Step k: wait until stage k+1 has landed, barrier (stage k+1 visible to
   // every wave; every wave is done reading stage k, whose buffer now takes
@@ -311,7 +335,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // sets into one and serialize the reads behind the MFMAs).
   constexpr int RGROUPS = LOADS * 3 / 4;
   constexpr int MPG = Cfg::NMFMA / LOADS;
-  auto step = [&](int k, int set) {
+  auto step = [&](int k, int set, auto f16) {
     wait_vmcnt<(STAGES - 2) * LOADS>();
     lds_barrier();
     const int8_t* rbase = stages + ((k + 1) % STAGES) * Cfg::STAGE_BYTES;
@@ -322,12 +346,46 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
       for (int r = 0; r < Cfg::NREADS; ++r)
         if (r * RGROUPS / Cfg::NREADS == g) read_one(rbase, r, set ^ 1);
 #pragma unroll
-      for (int m = g * MPG; m < (g + 1) * MPG; ++m) mfma_one(m, set);
+      for (int m = g * MPG; m < (g + 1) * MPG; ++m) mfma_one(m, set, f16);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
+  // sw/127 (and bias) of the 16 features lane (l32, lhi) holds in slice a.
+  auto load_fw = [&](int a, float* fw, float* bv) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int fl = wn * WN + a * 32 + 8 * g + 4 * lhi;
+      const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
+      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
+      if (bv) {
+        const float4 b4 = *reinterpret_cast<const float4*>(s_bias + fl);
+        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
+      }
+    }
+  };
+
+  // With every column an outlier column the int8 codes are all zero and the
+  // int8 segment is skipped.
+  const int nk = (seg2 && n_o == K) ? 0 : (K + BK - 1) / BK;
+  const std::integral_constant<bool, false> kInt8{};
+  const std::integral_constant<bool, true> kF16{};
+  // Runs main-loop steps 0 .. steps-1 over the current operands, after
+  // stages 0 .. STAGES-1 have been issued.
+  auto run_steps = [&](int steps, auto f16) {
+    wait_vmcnt<(STAGES - 1) * LOADS>();
+    lds_barrier();
+    read_frags(0, 0);
+    step(0, 0, f16);
+    if (!decltype(f16)::value && n_o > 0 && !seg2) store_outliers();   // read by the epilogue
+    int k = 1;
+    for (; k + 1 < steps; k += 2) {
+      step(k, 1, f16);
+      step(k + 1, 0, f16);
+    }
+    if (k < steps) step(k, 1, f16);
+    wait_vmcnt<0>();
+  };
   // Prologue, one memory round trip deep: the row / column factors are read
   // into registers, the first STAGES stages are issued, then the gathers of
   // the first outlier chunk; the factors go to LDS as soon as they arrive
@@ -341,9 +399,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     fw_mine = (tid < BN && n < N) ? sw[n] : 0.0f;
     b_mine = (bias && tid < BN && n < N) ? h2f(bias[n]) : 0.0f;
   }
+  if (nk > 0) {
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(s);
-  if (n_o > 0) fetch_outliers(0);
+    for (int s = 0; s < STAGES; ++s) issue_stage(s);
+  }
+  if (n_o > 0 && !seg2) fetch_outliers(0);
   if (Y) {
     if (tid < BM) s_ax[tid] = ax_mine / 127.0f;
     if (tid < BN) {
@@ -351,18 +411,37 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
       s_bias[tid] = b_mine;
     }
   }
-  wait_vmcnt<(STAGES - 1) * LOADS>();
-  lds_barrier();
-  read_frags(0, 0);
-  step(0, 0);
-  if (n_o > 0) store_outliers();   // read by the epilogue, after later barriers
-  int k = 1;
-  for (; k + 1 < nk; k += 2) {
-    step(k, 1);
-    step(k + 1, 0);
+  if (nk > 0) run_steps(nk, kInt8);
+
+  if (seg2) {
+    // Every wave is done with the int8 stages; the factors are in LDS.
+    lds_barrier();
+    // Dequantize in place, C * (sx/127) * (sw/127) in fp32 (the same
+    // expression as the epilogue's), then the outlier segment adds
+    // sum_t Xo[i, t] * Wo[j, t] onto it.
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      float fw[16];
+      load_fw(a, fw, nullptr);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        const float ax = s_ax[wm * WM + b * 32 + l32];
+        v16f32 y;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax * fw[r];
+        acc[a][b] = __builtin_bit_cast(v16i32, y);
+      }
+    }
+    const int seg_rows =
+        loads_w ? (int)min<int64_t>(BN, N - n0) : (int)min<int64_t>(BM, M - m0);
+    const uint16_t* seg_base = loads_w ? Wo + n0 * ldo : Xo + m0 * ldo;
+    rstride = rowbytes = (int)(2 * ldo);
+    rsrc = make_rsrc(seg_base, (uint32_t)seg_rows * (uint32_t)rowbytes);
+    set_offsets();
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_stage(s);
+    run_steps(rowbytes / BK, kF16);
   }
-  if (k < nk) step(k, 1);
-  wait_vmcnt<0>();
   // every wave is done with the stage buffers before the epilogue reuses them
   if (Y) lds_barrier();
 
@@ -451,18 +530,6 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  auto load_fw = [&](int a, float* fw, float* bv) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int fl = wn * WN + a * 32 + 8 * g + 4 * lhi;
-      const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
-      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
-      if (bv) {
-        const float4 b4 = *reinterpret_cast<const float4*>(s_bias + fl);
-        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
-      }
-    }
-  };
   // LDS outlier fragments: 8 fp16 (t = 8*lhi .. 8*lhi+7) of row l32 of a
   // 32-row slice; same lane -> t assignment on the weight and token side.
   auto wo_frag = [&](int a) -> v8f16 {
@@ -504,19 +571,25 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
     float fw[16], bv[16];
     load_fw(a, fw, bias ? bv : nullptr);
     v16f32 y[TM];
+    if (seg2) {
+      // already dequantized, with the outlier product added
 #pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const float ax = s_ax[wm * WM + b * 32 + l32];
+      for (int b = 0; b < TM; ++b) y[b] = __builtin_bit_cast(v16f32, acc[a][b]);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
+      for (int b = 0; b < TM; ++b) {
+        const float ax = s_ax[wm * WM + b * 32 + l32];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
+      }
     }
-    if (n_o > 0) {
+    if (n_o > 0 && !seg2) {
       const v8f16 wa = wo_frag(a);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
         y[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xo_frag(b), y[b], 0, 0, 0);
     }
-    for (int t0 = 16; t0 < n_o; t0 += 16) {
+    for (int t0 = 16; t0 < (seg2 ? 0 : n_o); t0 += 16) {
       const v8f16 wa = wo_frag_g(a, t0);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
@@ -538,14 +611,14 @@ template <class Cfg>
 hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                         hipStream_t s) {
+                         const uint16_t* Wo, hipStream_t s) {
   const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
   if (C)
     hipLaunchKernelGGL((k_gemm_i8<Cfg, true>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
   else
     hipLaunchKernelGGL((k_gemm_i8<Cfg, false>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
   return hipGetLastError();
 }
 
@@ -561,15 +634,15 @@ constexpr int64_t kLargeTileMin = I8MM_LARGE_TILE_MIN;
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                       hipStream_t s) {
+                       const uint16_t* Wo, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (gemv_applies(M)) return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
   // 256 x 256 tiles when they give every CU at least one; otherwise the
   // 128 x 128 tiles (four times as many, two blocks per CU).
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_large >= kLargeTileMin)
-    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
-  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
+    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, s);
+  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, s);
 }
 
 }  // namespace i8mm

@@ -16,7 +16,10 @@
 
 #include <cmath>
 
+#include <algorithm>
+
 #include "device_common.h"
+#include "i8mm.h"
 #include "launchers.h"
 
 namespace i8mm {
@@ -39,18 +42,22 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t val
 // >= tau ([HF-blog] "Inside the MatMul": magnitude 6 or greater; [Summary]
 // "The full picture" step 1). NaN patterns exceed every threshold pattern, so
 // a column holding NaN is flagged too and NaN never enters the int8 path.
-// Flag bits are merged into the (pre-zeroed) bitmap with atomicOr, issued
-// only for chunks that hold an outlier; OR is order-free.
+// Flag bits are merged into the (pre-zeroed) bitmap with atomicOr: the four
+// lanes of a 32-column word and the four waves of the block are OR-ed first,
+// and the atomic is issued only when it sets a bit the word does not have yet
+// (with many outlier columns most words fill early, and every block would
+// otherwise hit the same few words). OR is order-free.
 __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restrict__ X, int64_t M,
                                                        int64_t K, uint32_t tau16, int rows_per_block,
                                                        uint32_t* __restrict__ bitmap) {
+  __shared__ uint32_t s_word[4][16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
-  if (col0 >= K) return;
+  const bool col_ok = col0 < K;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(M, r0 + (int64_t)rows_per_block);
-  const uint16_t* base = X + col0;
+  const int64_t r1 = col_ok ? min(M, r0 + (int64_t)rows_per_block) : r0;
+  const uint16_t* base = X + (col_ok ? col0 : 0);
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   u16x2 mx[4] = {u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}};
   auto fold = [&](const uint4& v) {
@@ -76,7 +83,21 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
     mask |= ((uint32_t)mx[i][0] >= tau16 ? 1u : 0u) << (2 * i);
     mask |= ((uint32_t)mx[i][1] >= tau16 ? 1u : 0u) << (2 * i + 1);
   }
-  if (mask) atomicOr(&bitmap[col0 >> 5], mask << (col0 & 31));
+  if (!col_ok) mask = 0;   // (with threshold 0 an empty max would pass)
+  uint32_t word = mask << (col0 & 31);
+  word |= (uint32_t)__shfl_xor((int)word, 1, kWave);
+  word |= (uint32_t)__shfl_xor((int)word, 2, kWave);
+  if ((lane & 3) == 0) s_word[wave][lane >> 2] = word;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const uint32_t w = s_word[0][threadIdx.x] | s_word[1][threadIdx.x] | s_word[2][threadIdx.x] |
+                       s_word[3][threadIdx.x];
+    const int64_t widx = (int64_t)blockIdx.x * 16 + threadIdx.x;
+    if (w && widx * 32 < K) {
+      const uint32_t cur = __atomic_load_n(&bitmap[widx], __ATOMIC_RELAXED);
+      if ((cur & w) != w) atomicOr(&bitmap[widx], w);
+    }
+  }
 }
 
 // Exclusive prefix of popcount over the bitmap words, in LDS. Returns the
@@ -212,13 +233,16 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   auto strip = [&](int64_t row, int64_t c, uint4& t) {
     const uint32_t om = outl8(c);
     if (om) {
-      if (Xo) {
+      const int64_t k0 = c * 8;
+      const int pos0 = Xo ? (int)spre[k0 >> 5] + __popc(sbm[k0 >> 5] & ((1u << (k0 & 31)) - 1u)) : 0;
+      if (Xo && om == 0xffu && (pos0 & 7) == 0) {
+        // 8 outlier columns in a row land at 8 consecutive aligned positions
+        st16(Xo + row * ld + pos0, t);
+      } else if (Xo) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if ((om >> e) & 1u) {
-            const int64_t k = c * 8 + e;
-            const uint32_t w = sbm[k >> 5];
-            const int pos = (int)spre[k >> 5] + __popc(w & ((1u << (k & 31)) - 1u));
+            const int pos = pos0 + __popc(om & ((1u << e) - 1u));
             Xo[row * ld + pos] = (uint16_t)half_of(t, e);
           }
         }
@@ -313,6 +337,63 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   }
 }
 
+// Recovered fp16 weight columns of the outlier columns, for the GEMM's
+// outlier segment ([HF-blog] "Usage": the fp16 weights of the outlier matmul
+// come back from CB * SCB / 127, per output row):
+//   Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127))  for t < n,
+//   +0.0 for n <= t < LD(n), rows LD(n) halfs apart.
+// n is read on the device; with 16 or fewer outlier columns the GEMM stages
+// them itself and this does nothing. One block per (row, 2048-column chunk)
+// task. The value depends only on the code q and the row, and is odd in q
+// (each of the three roundings is symmetric), so the block computes the
+// values of q = 0..128 with the exact arithmetic into LDS, then each thread
+// builds 8 consecutive columns by lookup (sign bit from the code) and stores
+// them as one 16-byte write.
+constexpr int kRecoverCols = 2048;   // columns per block: 256 threads x 8
+__global__ __launch_bounds__(256) void k_recover_outlier_w(
+    const int8_t* __restrict__ Wq, const float* __restrict__ sw, int64_t N, int64_t K,
+    const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
+    uint16_t* __restrict__ Wo) {
+  __shared__ uint16_t s_lut[130];   // q = 0..128 (-128 is a valid int8)
+  const int n = *n_out;
+  if (n <= 16) return;
+  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
+  const int64_t chunks = (ld + kRecoverCols - 1) / kRecoverCols;
+  const int tid = threadIdx.x;
+  for (int64_t task = blockIdx.x; task < N * chunks; task += gridDim.x) {
+    const int64_t j = task / chunks;
+    const int64_t t0 = (task - j * chunks) * kRecoverCols + (int64_t)tid * 8;
+    // this thread's column indices and codes are fetched before the table
+    // is built, so their latency overlaps it
+    int c[8];
+    if (t0 + 8 <= n) {
+      const uint4 c0 = ld16(cols + t0), c1 = ld16(cols + t0 + 4);
+      c[0] = (int)c0.x; c[1] = (int)c0.y; c[2] = (int)c0.z; c[3] = (int)c0.w;
+      c[4] = (int)c1.x; c[5] = (int)c1.y; c[6] = (int)c1.z; c[7] = (int)c1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = t0 + e < n ? cols[t0 + e] : -1;
+    }
+    const int8_t* row = Wq + j * K;
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = c[e] >= 0 ? (int)row[c[e]] : 0;
+    __syncthreads();   // the previous task's lookups are done
+    if (tid <= 128) s_lut[tid] = f2h(((float)tid * sw[j]) / 127.0f);
+    __syncthreads();
+    if (t0 < ld) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mag = s_lut[q[e] < 0 ? -q[e] : q[e]];
+        h[e] = c[e] >= 0 ? (mag | (q[e] < 0 ? 0x8000u : 0u)) : 0u;
+      }
+      st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                        h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
+    }
+  }
+}
+
 // Exact-erf GELU in fp32 (activation between the two layers of an MLP block).
 __global__ void k_gelu(const uint16_t* __restrict__ X, int64_t count, uint16_t* __restrict__ Y) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -403,6 +484,18 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* 
   if (per_lane <= 24) return launch_rows_t<24>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
   if (per_lane <= 32) return launch_rows_t<32>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
   return launch_rows_t<0>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+}
+
+hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N, int64_t K,
+                                    const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
+                                    hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  // enough blocks for one (row, column chunk) task each at the largest n
+  const int64_t max_tasks = N * ((I8MM_OUTLIER_LD(K) + kRecoverCols - 1) / kRecoverCols);
+  const int64_t blocks = std::min<int64_t>(max_tasks, 2048);
+  hipLaunchKernelGGL(k_recover_outlier_w, dim3((unsigned)blocks), dim3(256), 0, s, Wq, sw, N, K,
+                     cols, n_out, Wo);
+  return hipGetLastError();
 }
 
 hipError_t launch_gelu(const uint16_t* X, int64_t count, uint16_t* Y, hipStream_t s) {

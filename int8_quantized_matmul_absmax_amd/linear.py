@@ -68,7 +68,7 @@ class Int8Linear(torch.nn.Module):
             raise TypeError("input must be fp16")
         x = x.contiguous()
         M = x.numel() // self.in_features
-        need = ops.workspace_bytes(M, self.in_features)
+        need = ops.workspace_bytes(M, self.in_features, self.out_features)
         if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
             self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
         return ops.linear_int8_mixed(x, self.Wq, self.sw, self.bias, self.threshold, self._ws)

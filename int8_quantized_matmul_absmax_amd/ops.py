@@ -135,9 +135,14 @@ def int8_mm_dequant(Xq, Wq, sx, sw, Xo=None, cols=None, n=None, bias=None, want_
     return Y if want_y else C
 
 
-def workspace_bytes(M, K):
+def workspace_bytes(M, K, N=None):
+    """Workspace bytes of linear_int8_mixed for M tokens and K features; with N
+    (output features) given, the size that also enables the fast path for
+    many outlier columns."""
     lib = _lib.load_library()
-    return int(lib.linear_int8_mixed_workspace_bytes(int(M), int(K)))
+    if N is None:
+        return int(lib.linear_int8_mixed_workspace_bytes(int(M), int(K)))
+    return int(lib.linear_int8_mixed_workspace_bytes_many_outliers(int(M), int(K), int(N)))
 
 
 def workspace_offsets(M, K):
@@ -165,8 +170,8 @@ def linear_int8_mixed(X, Wq, sw, bias=None, threshold=DEFAULT_THRESHOLD, workspa
     if bias is not None:
         _need(bias, "bias", torch.float16, 1)
     dev = X.device
-    need = workspace_bytes(M, K)
     if workspace is None:
+        need = workspace_bytes(M, K, N)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, 1)

@@ -125,7 +125,8 @@ def test_mlp_sweep_per_layer(gpu, n_in):
     Wq2_ref, sw2_ref = O.quantize_weight_rows(W2)
     assert np.array_equal(host(Wq2), Wq2_ref)
     K2 = G_ref.shape[1]
-    ws = torch.empty((ops.workspace_bytes(M, K2),), dtype=torch.uint8, device="cuda")
+    N2 = Wq2.shape[0]
+    ws = torch.empty((ops.workspace_bytes(M, K2, N2),), dtype=torch.uint8, device="cuda")
     Y2 = ops.linear_int8_mixed(dev(G_ref), Wq2, sw2, None, 6.0, ws)
     torch.cuda.synchronize()
     v = ops.workspace_views(ws, M, K2)

@@ -282,6 +282,42 @@ def test_linear_edge_cases(gpu, case):
         assert ref["n"] >= int(case[1:])
 
 
+@pytest.mark.parametrize("case", ["n17", "n33", "n100", "all_columns", "large_tiles_n40",
+                                  "large_tiles_all"])
+def test_linear_many_outliers_fast_path(gpu, case):
+    """More than 16 outlier columns with the larger workspace: the recovered
+    outlier weights are materialized and the outlier product runs as a second
+    GEMM main loop (all columns outliers: the int8 loop is skipped). Checked
+    against the oracle, and bit for bit against the small-workspace path,
+    which adds the same fp16 MFMA products in the same order in the epilogue."""
+    note("linear many outliers %s" % case)
+    rng = np.random.default_rng(300 + len(case))
+    large = case.startswith("large_tiles")
+    M, K, N = (4100, 528, 4100) if large else (200, 1040, 300)
+    X = synth.normal_f16(rng, (M, K), 1.0)
+    W = synth.normal_f16(rng, (N, K), 0.05)
+    tau = 6.0
+    if case.endswith("all") or case == "all_columns":
+        tau = 0.0
+    else:
+        n_plant = int(case.split("n")[-1])
+        synth.plant_outlier_columns(rng, X, n_plant, 7.0, 30.0, (0.05, 0.6))
+    bias = synth.normal_f16(rng, (N,), 0.5)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, tau, bias)
+    assert ref["n"] > 16
+    ops = _ops(gpu)
+    ws_big = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    ws_small = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    Xd, Wqd, swd, bd = dev(X), dev(Wq), dev(sw), dev(bias)
+    Y_fast = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_big)
+    Y_slow = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_small)
+    torch.cuda.synchronize()
+    _check_intermediates(gpu, ops.workspace_views(ws_big, M, K), X, ref)
+    assert y_err(host(Y_fast), ref["Y"]) <= Y_TOL
+    assert np.array_equal(host(Y_fast).view(np.uint16), host(Y_slow).view(np.uint16))
+
+
 def test_linear_large_tiles_ragged(gpu):
     """A shape with enough 256 x 256 tiles for the large-tile GEMM, ragged in M
     and N, with outlier columns and a bias."""
