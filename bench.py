@@ -267,6 +267,159 @@ def _summarize_trace(trace_dir):
     print("\n".join(out))
 
 
+SWEEP_FILE = os.path.join(ROOT, "profiles", "layer_all_configs_sweep.md")
+
+
+def _graph_time_us(call, reps, replays=20):
+    """Per-call GPU time of `call` (a no-argument function that launches on
+    torch's current stream): `reps` calls captured in one HIP graph, the graph
+    replayed `replays` times between HIP events, so host launch overhead is
+    out of the figure. Returns (us per call, outputs identical on every
+    replay)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ref = call()
+        torch.cuda.synchronize()
+        ref = ref.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            outs = [call() for _ in range(reps)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    same = True
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    same &= bool(torch.equal(outs[-1], ref))
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    end.synchronize()
+    same &= bool(torch.equal(outs[-1], ref))
+    return start.elapsed_time(end) * 1e3 / (replays * reps), same
+
+
+def _sweep():
+    """Every workload through linear_int8_mixed on one GPU; one JSON line per
+    case and a markdown summary under profiles/."""
+    import numpy as np
+    import torch
+    import int8_quantized_matmul_absmax_amd as i8
+    from int8_quantized_matmul_absmax_amd import synth
+    i8.ensure_built()
+    ops = i8.ops
+    torch.cuda.set_device(0)
+    rows = []
+
+    def emit(rec):
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+
+    def quantize(W):
+        return ops.int8_quantize_colwise_weight(torch.from_numpy(W).cuda())
+
+    # tiny layer and decode: graph-captured calls (host launch cost excluded),
+    # the weight rotated over copies beyond 2 x MALL for the decode shapes
+    for name, d in [("tiny 16x256->256", synth.tiny())] + [
+            ("decode M=%d 4096->4096" % m, synth.decode(m)) for m in (1, 4, 16)]:
+        X = torch.from_numpy(d["X"]).cuda()
+        M, K = d["X"].shape
+        Wq, sw = quantize(d["W"])
+        N = Wq.shape[0]
+        copies = max(1, min(40, (2 * MALL_BYTES) // max(Wq.numel(), 1) + 1))
+        Wqs = [Wq] + [Wq.clone() for _ in range(copies - 1)]
+        ws = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        state = {"i": 0}
+
+        def call():
+            state["i"] += 1
+            return ops.linear_int8_mixed(X, Wqs[state["i"] % copies], sw, None, 6.0, ws, Y)
+        us, same = _graph_time_us(call, reps=copies)
+        bytes_w = N * K + 4 * N
+        emit({"case": name, "M": M, "K": K, "N": N, "us_per_layer": round(us, 3),
+              "weight_stream_gbps": round(bytes_w / (us * 1e-6) / 1e9, 1),
+              "eff_tops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 4),
+              "timing": "hip graph of %d calls" % copies, "replays_identical": same})
+        del Wqs, ws, Y, X
+
+    def ev_us(fn, iters):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    # two-layer MLP block, per outlier density
+    for n_in in (0, 6, 32, 128, 512):
+        d = synth.mlp_sweep(n_in)
+        X = torch.from_numpy(d["X"]).cuda()
+        M, H = d["X"].shape
+        F = d["W1"].shape[0]
+        Wq1, sw1 = quantize(d["W1"])
+        Wq2, sw2 = quantize(d["W2"])
+        ws1 = torch.empty((ops.workspace_bytes(M, H, F),), dtype=torch.uint8, device="cuda")
+        ws2 = torch.empty((ops.workspace_bytes(M, F, H),), dtype=torch.uint8, device="cuda")
+        Y1 = torch.empty((M, F), dtype=torch.float16, device="cuda")
+        G = torch.empty_like(Y1)
+        Y2 = torch.empty((M, H), dtype=torch.float16, device="cuda")
+        ops.linear_int8_mixed(X, Wq1, sw1, None, 6.0, ws1, Y1)
+        ops.gelu_f16(Y1, G)
+        ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2)
+        torch.cuda.synchronize()
+        n1 = int(ops.workspace_views(ws1, M, H)["n"].cpu()[0])
+        n2 = int(ops.workspace_views(ws2, M, F)["n"].cpu()[0])
+        t1 = ev_us(lambda: ops.linear_int8_mixed(X, Wq1, sw1, None, 6.0, ws1, Y1), 20)
+        tg = ev_us(lambda: ops.gelu_f16(Y1, G), 20)
+        t2 = ev_us(lambda: ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2), 10)
+        fl = 2.0 * M * F * H
+        emit({"case": "mlp n_in=%d" % n_in, "M": M, "H": H, "F": F, "n_layer1": n1,
+              "n_layer2": n2, "us_layer1": round(t1, 2), "us_gelu": round(tg, 2),
+              "us_layer2": round(t2, 2), "eff_tops_layer1": round(fl / (t1 * 1e-6) / 1e12, 1),
+              "eff_tops_layer2": round(fl / (t2 * 1e-6) / 1e12, 1), "timing": "hip events"})
+        del Wq1, Wq2, ws1, ws2, Y1, G, Y2, X
+
+    # 175B-scale FFN layer
+    d = synth.ffn_175b()
+    X = torch.from_numpy(d["X"]).cuda()
+    M, K = d["X"].shape
+    W = torch.from_numpy(d["W"]).cuda()
+    N = W.shape[0]
+    del d
+    Wq, sw = ops.int8_quantize_colwise_weight(W)
+    tq = ev_us(lambda: ops.int8_quantize_colwise_weight(W, Wq, sw), 5)
+    del W
+    ws = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    t = ev_us(lambda: ops.linear_int8_mixed(X, Wq, sw, None, 6.0, ws, Y), 5)
+    emit({"case": "ffn 175B-scale", "M": M, "K": K, "N": N, "us_per_layer": round(t, 1),
+          "eff_tops": round(2.0 * M * N * K / (t * 1e-6) / 1e12, 1),
+          "int8_peak_frac": round(2.0 * M * N * K / (t * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+          "weight_quant_us": round(tq, 1),
+          "weight_quant_gbps": round((3.0 * N * K + 4.0 * N) / (tq * 1e-6) / 1e9, 1),
+          "timing": "hip events"})
+
+    out = ["# linear_int8_mixed on every workload (one MI355X)", "",
+           "Command (from the repository root):", "", "    python3 bench.py --sweep", "",
+           "Decode and tiny layers: one HIP graph of many calls (weight rotated over copies "
+           "beyond 2 x the 256 MB MALL), replayed; others: HIP events around back-to-back "
+           "calls. Times are per whole layer call (all kernels).", ""]
+    for r in rows:
+        out.append("- `" + json.dumps(r) + "`")
+    with open(SWEEP_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +433,8 @@ def main():
     ap.add_argument("--write-counters", metavar="PMC_DIR",
                     help="write the stored GEMM traffic figure from rocprofv3 counter runs "
                          "(no GPU needed) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the layer on every workload and write the summary under profiles/")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write the committed kernel-trace summary from a rocprofv3 run "
                          "(no GPU needed) and exit")
@@ -298,6 +453,9 @@ def main():
 
     if args.copy_probe:
         _copy_probe()
+        return
+    if args.sweep:
+        _sweep()
         return
 
     import numpy as np

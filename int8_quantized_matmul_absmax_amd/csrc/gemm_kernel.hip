@@ -148,9 +148,17 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
   tn = in / gsz;
 }
 
-// WITH_C: also write the raw int32 accumulators (parity mode); a separate
-// instantiation so the fp16 path carries none of that code.
-template <class Cfg, bool WITH_C>
+// Kernel modes, separate instantiations so that each carries only its code
+// (register pressure):
+//   kPlain   fp16 output; outlier product in the epilogue. Given Wo, it
+//            returns at once when there are more than 16 outlier columns
+//            (kOutlierSeg does those).
+//   kInt32   kPlain that also writes the raw int32 accumulators (parity mode).
+//   kOutlierSeg  only for more than 16 outlier columns with Wo given
+//            (returns at once otherwise): the outlier product as a second
+//            main-loop segment.
+enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2 };
+template <class Cfg, int MODE>
 __global__ __launch_bounds__(256) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
@@ -188,7 +196,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // [N, ldo] fp16): the outlier product runs as a second main-loop segment
   // over the outlier columns (fp16 MFMA on Wo and Xo through the same stage
   // pipeline) instead of in the epilogue.
-  const bool seg2 = !WITH_C && Wo != nullptr && n_o > 16;
+  constexpr bool WITH_C = MODE == kInt32;
+  const bool many = Wo != nullptr && n_o > 16;
+  if (MODE == kOutlierSeg ? !many : many) return;   // the other mode's case
+  constexpr bool seg2 = MODE == kOutlierSeg;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
   static_assert(BN <= kThreads && BM <= kThreads, "at most one row of each outlier tile per thread");
@@ -613,12 +624,22 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                          const uint16_t* Wo, hipStream_t s) {
   const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
-  if (C)
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, true>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
-  else
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, false>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
+  if (C) {
+    // parity mode: the epilogue outlier path only
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, nullptr);
+    return hipGetLastError();
+  }
+  // The outlier count is only known on the device: with Wo given both modes
+  // are launched and the one whose case it is not returns at once.
+  hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+                     Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
+  if (Wo) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
+                       Xq, Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
+  }
   return hipGetLastError();
 }
 
