@@ -253,8 +253,9 @@ int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
   int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
   uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
   const int64_t nwords = (K + 31) / 32;
+  const uint32_t tau16 = i8mm::fp16_threshold_pattern(threshold);
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
-  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, i8mm::fp16_threshold_pattern(threshold), bitmap, s), fn));
+  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, tau16, bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
   // With room for it, the recovered outlier weight columns are materialized
   // for the tiled GEMM (the kernel does nothing for 16 or fewer columns).

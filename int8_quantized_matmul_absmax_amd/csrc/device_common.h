@@ -38,6 +38,30 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Wave-wide maximum with DPP moves (VALU, no LDS round trips): a running
+// maximum over each 16-lane row by row_shr 1, 2, 4, 8 leaves the row's
+// maximum in its last lane; the four row maxima are read out as scalars.
+// The result is uniform across the wave.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  // row_shr:n is DPP control 0x110 + n; bound_ctrl makes shifted-in lanes 0
+  // (the identity of an unsigned maximum)
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);
+  v = v > t ? v : t;
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {

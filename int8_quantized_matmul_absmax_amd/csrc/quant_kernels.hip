@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
       }
     }
     uint32_t mx = m2[0] > m2[1] ? m2[0] : m2[1];
-    mx = wave_max_u32(mx);
+    mx = wave_max_u32_dpp(mx);
     const float a = h2f(mx);
     const float s = a != 0.0f ? 127.0f / a : 0.0f;
     if (Xq) {

@@ -207,6 +207,7 @@ def _check_intermediates(gpu, views, X, ref):
     ld = _ops(gpu).outlier_ld(n)
     Xo = host(views["Xo"])[: M * ld].reshape(M, ld)
     assert np.array_equal(Xo[:, :n].view(np.uint16), X[:, ref["cols"]].view(np.uint16))
+    assert not np.any(Xo[:, n:ld].view(np.uint16))   # pad columns hold +0.0
 
 
 @pytest.mark.parametrize("case", ["tiny", "decode1", "decode4", "decode16", "medium_ragged",
@@ -352,6 +353,40 @@ def test_linear_token_counts(gpu, M):
                                   want_int32=True)
     torch.cuda.synchronize()
     assert np.array_equal(host(C), O.int32_accumulators(ref["Xq"], Wq))
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("case", ["mixed", "tau_zero", "no_outliers"])
+def test_linear_few_tokens_x_side(gpu, M, case):
+    """Few tokens: bitmap, cols, n, codes, scales and gathered outliers against
+    the oracle, with K not a multiple of 32, an exact +-6.0, a NaN column, an
+    inf column, threshold 0 (every column) and a case with no outlier column."""
+    note("few tokens x side M=%d %s" % (M, case))
+    rng = np.random.default_rng(500 + M)
+    K = 528
+    X = synth.normal_f16(rng, (M, K), 1.0)
+    W = synth.normal_f16(rng, (77, K), 0.05)
+    tau = 6.0
+    if case == "mixed":
+        X[0, 3] = 6.0
+        X[M - 1, 200] = -6.0
+        X[0, 517] = np.float16(np.inf)
+        X[M // 2, 40] = np.float16(np.nan)
+        X[:, 301] = 9.5
+    elif case == "tau_zero":
+        tau = 0.0
+    else:
+        X = np.clip(X.astype(np.float32), -5.0, 5.0).astype(np.float16)
+    Wq, sw = O.quantize_weight_rows(W)
+    with np.errstate(invalid="ignore"):   # the planted NaN reaches the oracle's sums
+        ref = O.linear_int8_mixed(X, Wq, sw, tau)
+    Y, views = _run_linear(gpu, X, Wq, sw, tau)
+    _check_intermediates(gpu, views, X, ref)
+    if case == "mixed":
+        assert {3, 40, 200, 301, 517} <= set(ref["cols"].tolist())
+        # the NaN and inf reach Y only through the fp16 outlier product
+        return
+    assert y_err(Y, ref["Y"]) <= Y_TOL
 
 
 def test_linear_is_deterministic(gpu):
