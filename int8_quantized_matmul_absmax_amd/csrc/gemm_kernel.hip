@@ -68,13 +68,16 @@ namespace {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;
 
-template <int BM_, int BN_, int BK_, int STAGES_>
+// WAVES_M x 2 wavefronts per block (WAVES_M = 2: one per SIMD, each wave
+// 128 x 128 of a 256 x 256 tile; WAVES_M = 4: two per SIMD, 64 x 128 each).
+template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_ = 2>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
-  static constexpr int WM = BM / 2;                 // tokens per wave
-  static constexpr int WN = BN / 2;                 // features per wave
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = 2, WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M;           // tokens per wave
+  static constexpr int WN = BN / WAVES_N;           // features per wave
   static constexpr int TM = WM / 32;                // MFMA tiles per wave, token dim
   static constexpr int TN = WN / 32;                // MFMA tiles per wave, feature dim
   static constexpr int KS = BK / 32;                // MFMA k-steps per stage
@@ -82,7 +85,7 @@ struct GemmCfg {
   static constexpr int ROWS = BM + BN;              // LDS rows per stage
   static constexpr int STAGE_BYTES = ROWS * BK;
   static constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wave-wide load fills
-  static constexpr int LOADS = ROWS / ROWS_PER_LOAD / 4;  // loads per wave per stage
+  static constexpr int LOADS = ROWS / ROWS_PER_LOAD / WAVES;  // loads per wave per stage
   static constexpr int NREADS = KS * (TN + TM);     // fragment reads per stage
   static constexpr int NMFMA = KS * TN * TM;        // MFMAs per stage
   // LDS: [scales: sx/127 (BM), sw/127 (BN), bias (BN) floats]
@@ -159,7 +162,7 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
 //            main-loop segment.
 enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2 };
 template <class Cfg, int MODE>
-__global__ __launch_bounds__(256) void k_gemm_i8(
+__global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % Cfg::WAVES_N, wm = wave / Cfg::WAVES_N;
   const int l32 = lane & 31, lhi = lane >> 5;
 
   int tile_m, tile_n;
@@ -202,7 +205,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   constexpr bool seg2 = MODE == kOutlierSeg;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
-  static_assert(BN <= kThreads && BM <= kThreads, "at most one row of each outlier tile per thread");
+  static_assert(BN <= Cfg::THREADS && BM <= Cfg::THREADS,
+                "at most one row of each outlier tile per thread");
   int wq_g[16];
   float sw_mine = 0.0f;
   uint4 xo_mine[2];
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
   // Wave-wide load j of wave w fills LDS rows R0 .. R0+RPL-1 of the stage,
   // lane l -> row R0 + l/4, physical chunk l%4, logical chunk (l%4)^f(row).
-  const bool loads_w = wave < 2;
+  const bool loads_w = wave < Cfg::WAVES / 2;
   const int op_rows_valid =
       loads_w ? (int)min<int64_t>(BN, N - n0) : (int)min<int64_t>(BM, M - m0);
   const int8_t* op_base = loads_w ? Wq + n0 * K : Xq + m0 * K;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // (the int8 codes: K and K; the outlier segment: 2 * ldo and 2 * ldo).
   __amdgpu_buffer_rsrc_t rsrc = make_rsrc(op_base, (uint32_t)op_rows_valid * (uint32_t)K);
   int rstride = K, rowbytes = K;
-  const int row_first = (loads_w ? 0 : BN) + (wave & 1) * (LOADS * RPL);
+  const int row_first = (loads_w ? 0 : BN) + (wave % (Cfg::WAVES / 2)) * (LOADS * RPL);
   // Lane offsets: load j covers rows row_first + 16j + lane/4; the swizzle
   // key of those rows depends on j only through its parity.
   int voff[2], lchunk16[2];
@@ -404,7 +408,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // the first main-loop step, so their latency overlaps it.
   float ax_mine = 0.0f, fw_mine = 0.0f, b_mine = 0.0f;
   if (Y) {
-    static_assert(BM <= kThreads && BN <= kThreads, "at most one factor of each kind per thread");
+    static_assert(BM <= Cfg::THREADS && BN <= Cfg::THREADS,
+                  "at most one factor of each kind per thread");
     const int64_t m = m0 + tid, n = n0 + tid;
     ax_mine = (tid < BM && m < M) ? sx[m] : 0.0f;
     fw_mine = (tid < BN && n < N) ? sw[n] : 0.0f;
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(
   // 128-byte row segment of Y: write misses reach memory as full lines
   // rather than as 16-byte pieces of 32 different rows.
   constexpr int OUT_ROW = 64 * 2 + 16;               // bytes per staged row (+ pad)
-  static_assert(4 * WM * OUT_ROW <= STAGES * Cfg::STAGE_BYTES, "output staging fits");
+  static_assert(Cfg::WAVES * WM * OUT_ROW <= STAGES * Cfg::STAGE_BYTES, "output staging fits");
   static_assert(TN % 2 == 0, "slices are stored in pairs");
   int8_t* s_out = stages + wave * (WM * OUT_ROW);
   const bool n8 = (N & 7) == 0;
@@ -626,24 +631,27 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
   const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
   if (C) {
     // parity mode: the epilogue outlier path only
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
                        Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, nullptr);
     return hipGetLastError();
   }
   // The outlier count is only known on the device: with Wo given both modes
   // are launched and the one whose case it is not returns at once.
-  hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), dim3((unsigned)tiles), dim3(kThreads), 0, s, Xq,
+  hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
                      Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
   if (Wo) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s,
                        Xq, Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
   }
   return hipGetLastError();
 }
 
-using CfgLarge = GemmCfg<256, 256, 64, 4>;
+#ifndef I8MM_LARGE_WAVES_M
+#define I8MM_LARGE_WAVES_M 4
+#endif
+using CfgLarge = GemmCfg<256, 256, 64, 4, I8MM_LARGE_WAVES_M>;
 using CfgSmall = GemmCfg<128, 128, 64, 4>;
 #ifndef I8MM_LARGE_TILE_MIN
 #define I8MM_LARGE_TILE_MIN 256
