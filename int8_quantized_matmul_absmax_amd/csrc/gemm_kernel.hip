@@ -88,13 +88,16 @@ struct GemmCfg {
   static constexpr int LOADS = ROWS / ROWS_PER_LOAD / WAVES;  // loads per wave per stage
   static constexpr int NREADS = KS * (TN + TM);     // fragment reads per stage
   static constexpr int NMFMA = KS * TN * TM;        // MFMAs per stage
-  // LDS: [scales: sx/127 (BM), sw/127 (BN), bias (BN) floats]
-  //      [outlier tiles: Wo (BN x 16) and Xo (BM x 16) fp16][STAGES stages]
+  // LDS: STAGES stage buffers; after the main loop the same bytes hold the
+  // epilogue's [scales][outlier tiles][output staging].
+  static constexpr int STAGE0 = 0;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
   static constexpr int OUTL0 = SCALE_BYTES;
   static constexpr int OUTL_BYTES = (BN + BM) * 16 * 2;
-  static constexpr int STAGE0 = (OUTL0 + OUTL_BYTES + 1023) / 1024 * 1024;
-  static constexpr int LDS_BYTES = STAGE0 + STAGES * STAGE_BYTES;
+  static constexpr int OUT_ROW = 64 * 2 + 16;
+  static constexpr int OUT0 = (OUTL0 + OUTL_BYTES + 1023) / 1024 * 1024;
+  static_assert(OUT0 + WAVES * WM * OUT_ROW <= LDS_BYTES, "epilogue views fit the stages");
   static_assert(CPR == 4, "swizzle is written for 4 chunks per row");
   static_assert(BN % (4 * ROWS_PER_LOAD) == 0 && BM % (4 * ROWS_PER_LOAD) == 0, "split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -189,10 +192,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 
   // ---- outlier columns, 16 at a time: the recovered fp16 weight columns of
   // this block's BN features and the gathered fp16 activations of its BM
-  // tokens are staged in LDS. Chunk 0 is fetched before the stage loads are
-  // issued and written to LDS after them, so its latency overlaps the
-  // pipeline prologue; further chunks (more than 16 outlier columns) are
-  // staged in the epilogue.
+  // tokens are staged in LDS for the epilogue. Chunk 0 is gathered in the
+  // prologue, between the stage loads, and held in registers until the main
+  // loop has freed LDS; further chunks (more than 16 outlier columns) are
+  // read in the epilogue.
   const int n_o = (Xo && cols && n_out && Y) ? *n_out : 0;
   const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
   // More than 16 outlier columns with the recovered weights materialized (Wo
@@ -205,42 +208,51 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   constexpr bool seg2 = MODE == kOutlierSeg;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
-  static_assert(BN <= Cfg::THREADS && BM <= Cfg::THREADS,
-                "at most one row of each outlier tile per thread");
-  int wq_g[16];
-  float sw_mine = 0.0f;
-  uint4 xo_mine[2];
-  auto fetch_outliers = [&](int t0) {
-    const int64_t f = n0 + tid;
-    const bool f_ok = tid < BN && f < N;
-    sw_mine = f_ok ? sw[f] : 0.0f;
+  // Values held in registers from the prologue to the end of the main loop
+  // (the stage buffers fill all of LDS until then), split so that no thread
+  // holds more than nine: thread tid < BM keeps token m0 + tid's factor and
+  // its gathered outlier activations, thread BM + f feature n0 + f's factor,
+  // bias and gathered int8 outlier weight codes (four per register).
+  static_assert(BM + BN <= Cfg::THREADS, "one held row per thread");
+  const bool tok_side = tid < BM;   // uniform per wave
+  const int hr = tok_side ? tid : tid - BM;
+  const bool h_ok = tok_side ? m0 + hr < M : (hr < BN && n0 + hr < N);
+  uint32_t keep[9];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      // cols[t0 + t] is the same for every lane (a scalar load)
-      const int c = t0 + t < n_o ? __builtin_amdgcn_readfirstlane(cols[t0 + t]) : 0;
-      wq_g[t] = (f_ok && t0 + t < n_o) ? (int)Wq[f * K + c] : 0;
+  for (int i = 0; i < 9; ++i) keep[i] = 0;
+  auto fetch_outliers = [&]() {
+    if (!h_ok) return;
+    if (tok_side) {
+      const uint16_t* src = Xo + (m0 + hr) * ldo;
+      const uint4 x0 = ld16(src), x1 = ld16(src + 8);
+      keep[0] = x0.x; keep[1] = x0.y; keep[2] = x0.z; keep[3] = x0.w;
+      keep[4] = x1.x; keep[5] = x1.y; keep[6] = x1.z; keep[7] = x1.w;
+    } else {
+      const int8_t* row = Wq + (n0 + hr) * K;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        // cols[t] is the same for every lane (a scalar load)
+        const int c = t < n_o ? __builtin_amdgcn_readfirstlane(cols[t]) : 0;
+        const uint32_t q = t < n_o ? (uint8_t)row[c] : 0u;
+        keep[t / 4] |= q << (8 * (t % 4));
+      }
     }
-    const int64_t tok = m0 + tid;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      xo_mine[i] = (tid < BM && tok < M) ? ld16(Xo + tok * ldo + t0 + i * 8)
-                                          : make_uint4(0, 0, 0, 0);
   };
   auto store_outliers = [&]() {
-    uint32_t wpk[8];
+    if (tok_side) {
+      st16(s_xo + hr * 16, make_uint4(keep[0], keep[1], keep[2], keep[3]));
+      st16(s_xo + hr * 16 + 8, make_uint4(keep[4], keep[5], keep[6], keep[7]));
+    } else if (hr < BN) {
+      const float swf = __builtin_bit_cast(float, keep[4]);
+      uint32_t wpk[8];
 #pragma unroll
-    for (int t = 0; t < 16; t += 2) {
-      const uint32_t lo = f2h(((float)wq_g[t] * sw_mine) / 127.0f);
-      const uint32_t hi = f2h(((float)wq_g[t + 1] * sw_mine) / 127.0f);
-      wpk[t / 2] = lo | (hi << 16);
-    }
-    if (tid < BN) {
-      st16(s_wo + tid * 16, make_uint4(wpk[0], wpk[1], wpk[2], wpk[3]));
-      st16(s_wo + tid * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
-    }
-    if (tid < BM) {
-      st16(s_xo + tid * 16, xo_mine[0]);
-      st16(s_xo + tid * 16 + 8, xo_mine[1]);
+      for (int t = 0; t < 16; t += 2) {
+        const float q0 = (float)(int8_t)(keep[t / 4] >> (8 * (t % 4)));
+        const float q1 = (float)(int8_t)(keep[t / 4] >> (8 * (t % 4) + 8));
+        wpk[t / 2] = f2h((q0 * swf) / 127.0f) | (f2h((q1 * swf) / 127.0f) << 16);
+      }
+      st16(s_wo + hr * 16, make_uint4(wpk[0], wpk[1], wpk[2], wpk[3]));
+      st16(s_wo + hr * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
     }
   };
   // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
@@ -257,14 +269,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   const int row_first = (loads_w ? 0 : BN) + (wave % (Cfg::WAVES / 2)) * (LOADS * RPL);
   // Lane offsets: load j covers rows row_first + 16j + lane/4; the swizzle
   // key of those rows depends on j only through its parity.
-  int voff[2], lchunk16[2];
+  // The row-group and k offsets go in the scalar operand, which the hardware
+  // bounds check leaves out, so each lane tests its row and k chunk itself:
+  // kleft[p] = rowbytes - its chunk's byte offset, rleft[p] = valid rows -
+  // its row (both must stay positive).
+  int voff[2], kleft[2], rleft[2];
   auto set_offsets = [&]() {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = row_first + p * RPL + (lane >> 2);
       const int c = (lane & 3) ^ swz_key(r);
-      voff[p] = (r - (loads_w ? 0 : BN)) * rstride + c * 16;
-      lchunk16[p] = c * 16;
+      const int rl = r - (loads_w ? 0 : BN);
+      voff[p] = rl * rstride + c * 16;
+      kleft[p] = rowbytes - c * 16;
+      rleft[p] = op_rows_valid - rl;
     }
   };
   set_offsets();
@@ -272,15 +290,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   auto issue_load = [&](int kt, int j) {
     const int k0 = kt * BK;
     int8_t* sbase = stages + (kt % STAGES) * Cfg::STAGE_BYTES + row_first * BK;
-    const int off = (k0 + lchunk16[j & 1] < rowbytes)
-                        ? voff[j & 1] + (j & ~1) * RPL * rstride + k0
-                        : 0x7ffffff0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, off,
-                                             0, 0, 0);
+    const int soff = __builtin_amdgcn_readfirstlane((j & ~1) * RPL * rstride + k0);
+    const bool ok = k0 < kleft[j & 1] && (j & ~1) * RPL < rleft[j & 1];
+    const int vo = ok ? voff[j & 1] : 0x7ffffff0 - soff;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sbase + j * RPL * BK), 16, vo,
+                                             soff, 0, 0);
   };
-  auto issue_stage = [&](int kt) {
+  auto issue_pair = [&](int kt) {   // stages kt, kt + 1, row block by row block
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) issue_load(kt, j);
+    for (int j = 0; j < LOADS; ++j) {
+      issue_load(kt, j);
+      issue_load(kt + 1, j);
+    }
   };
 
   // ---- fragment read offsets (bytes inside a stage)
@@ -341,22 +362,35 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
   // Step k: wait until stage k+1 has landed, barrier (stage k+1 visible to
-  // every wave; every wave is done reading stage k, whose buffer now takes
-  // stage k+STAGES), then LOADS groups in a fixed order, each of one stage
-  // load, a few fragment reads of stage k+1 into the other register set, and
-  // NMFMA/LOADS MFMAs on stage k. The reads fill the first RGROUPS groups so
-  // they have landed by the next barrier's LDS wait; the scheduling barriers
-  // keep the compiler from regrouping them (which would force both register
-  // sets into one and serialize the reads behind the MFMAs).
+  // every wave; every wave is done reading stage k), then LOADS groups in a
+  // fixed order, each of one stage load, a few fragment reads of stage k+1
+  // into the other register set, and NMFMA/LOADS MFMAs on stage k.
+  // Loads go out two stages at a time: the steps k (even) and k+1 together
+  // issue stages k+4 and k+5, each step half of the rows of both, alternating
+  // between the two stages. Back-to-back loads of the same rows of two
+  // consecutive k-blocks fill whole 128-byte lines of each operand row, which
+  // the vector L1 merges, where a single stage fetches half lines. Stage k+5
+  // takes stage k's buffer and stage k+4 that of k-1, both read by the time
+  // of step k's barrier. The waits follow from the issue order: before an
+  // even step the youngest 2*LOADS loads (the last two steps') may still be
+  // in flight; before an odd step only the even step's LOADS and the last
+  // load of the pair before it, the other stage of that pair.
+  // The reads fill the first RGROUPS groups so they have landed by the next
+  // barrier's LDS wait; the scheduling barriers keep the compiler from
+  // regrouping them (which would force both register sets into one and
+  // serialize the reads behind the MFMAs).
+  static_assert(STAGES == 5, "the paired issue order is written for five stages");
   constexpr int RGROUPS = LOADS * 3 / 4;
   constexpr int MPG = Cfg::NMFMA / LOADS;
   auto step = [&](int k, int set, auto f16) {
-    wait_vmcnt<(STAGES - 2) * LOADS>();
+    if (set == 0) wait_vmcnt<2 * LOADS>(); else wait_vmcnt<LOADS + 1>();
     lds_barrier();
     const int8_t* rbase = stages + ((k + 1) % STAGES) * Cfg::STAGE_BYTES;
+    const int pair0 = set == 0 ? k + 4 : k + 3;
+    const int row_half = set == 0 ? 0 : LOADS / 2;
 #pragma unroll
     for (int g = 0; g < LOADS; ++g) {
-      issue_load(k + STAGES, g);
+      issue_load(pair0 + (g & 1), row_half + g / 2);
 #pragma unroll
       for (int r = 0; r < Cfg::NREADS; ++r)
         if (r * RGROUPS / Cfg::NREADS == g) read_one(rbase, r, set ^ 1);
@@ -386,13 +420,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   const std::integral_constant<bool, false> kInt8{};
   const std::integral_constant<bool, true> kF16{};
   // Runs main-loop steps 0 .. steps-1 over the current operands, after
-  // stages 0 .. STAGES-1 have been issued.
+  // stages 0 .. 3 have been issued (issue_pair(0), then issue_pair(2)); the
+  // first wait leaves in flight the second pair and at most one load before
+  // it (stage 1's last, or the last outlier gather), so stage 0 has landed.
   auto run_steps = [&](int steps, auto f16) {
-    wait_vmcnt<(STAGES - 1) * LOADS>();
+    wait_vmcnt<2 * LOADS + 1>();
     lds_barrier();
     read_frags(0, 0);
     step(0, 0, f16);
-    if (!decltype(f16)::value && n_o > 0 && !seg2) store_outliers();   // read by the epilogue
     int k = 1;
     for (; k + 1 < steps; k += 2) {
       step(k, 1, f16);
@@ -401,37 +436,40 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     if (k < steps) step(k, 1, f16);
     wait_vmcnt<0>();
   };
-  // Prologue, one memory round trip deep: the row / column factors are read
-  // into registers, the first STAGES stages are issued, then the gathers of
-  // the first outlier chunk; the factors go to LDS as soon as they arrive
-  // (they are older than the stage loads), the gathered outlier columns after
-  // the first main-loop step, so their latency overlaps it.
-  float ax_mine = 0.0f, fw_mine = 0.0f, b_mine = 0.0f;
-  if (Y) {
-    static_assert(BM <= Cfg::THREADS && BN <= Cfg::THREADS,
-                  "at most one factor of each kind per thread");
-    const int64_t m = m0 + tid, n = n0 + tid;
-    ax_mine = (tid < BM && m < M) ? sx[m] : 0.0f;
-    fw_mine = (tid < BN && n < N) ? sw[n] : 0.0f;
-    b_mine = (bias && tid < BN && n < N) ? h2f(bias[n]) : 0.0f;
-  }
-  if (nk > 0) {
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_stage(s);
-  }
-  if (n_o > 0 && !seg2) fetch_outliers(0);
-  if (Y) {
-    if (tid < BM) s_ax[tid] = ax_mine / 127.0f;
-    if (tid < BN) {
-      s_fw[tid] = fw_mine / 127.0f;
-      s_bias[tid] = b_mine;
+  // Prologue: the row / column factors are read into registers, then the
+  // first four stages are issued with the chunk-0 outlier gathers between
+  // stages 0-1 and 2-3; factors and gathers go to LDS after the main loop.
+  if (Y && h_ok) {
+    if (tok_side) {
+      keep[8] = __builtin_bit_cast(uint32_t, sx[m0 + hr]);
+    } else {
+      keep[4] = __builtin_bit_cast(uint32_t, sw[n0 + hr]);
+      if (bias) keep[5] = bias[n0 + hr];
     }
   }
+  // The outlier gathers go after stages 0-1 and before stages 2-3: the first
+  // wait (for stages 0-1) then covers them too, and no later wait counts them
+  // as younger than a stage it needs.
+  if (nk > 0) issue_pair(0);
+  if (n_o > 0 && !seg2) fetch_outliers();
+  if (nk > 0) issue_pair(2);
+  auto store_scales = [&]() {
+    if (Y) {
+      if (tok_side) {
+        s_ax[hr] = __builtin_bit_cast(float, keep[8]) / 127.0f;
+      } else if (hr < BN) {
+        s_fw[hr] = __builtin_bit_cast(float, keep[4]) / 127.0f;
+        s_bias[hr] = h2f((uint16_t)keep[5]);
+      }
+    }
+  };
   if (nk > 0) run_steps(nk, kInt8);
+  lds_barrier();   // every wave is done with the stage buffers
+  store_scales();
+  if (n_o > 0 && !seg2) store_outliers();
 
   if (seg2) {
-    // Every wave is done with the int8 stages; the factors are in LDS.
-    lds_barrier();
+    lds_barrier();   // the factors are in LDS
     // Dequantize in place, C * (sx/127) * (sw/127) in fp32 (the same
     // expression as the epilogue's), then the outlier segment adds
     // sum_t Xo[i, t] * Wo[j, t] onto it.
@@ -448,15 +486,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
         acc[a][b] = __builtin_bit_cast(v16i32, y);
       }
     }
-    const int seg_rows =
-        loads_w ? (int)min<int64_t>(BN, N - n0) : (int)min<int64_t>(BM, M - m0);
     const uint16_t* seg_base = loads_w ? Wo + n0 * ldo : Xo + m0 * ldo;
     rstride = rowbytes = (int)(2 * ldo);
-    rsrc = make_rsrc(seg_base, (uint32_t)seg_rows * (uint32_t)rowbytes);
+    rsrc = make_rsrc(seg_base, (uint32_t)op_rows_valid * (uint32_t)rowbytes);
     set_offsets();
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_stage(s);
+    lds_barrier();   // every wave has read its factors
+    issue_pair(0);
+    issue_pair(2);
     run_steps(rowbytes / BK, kF16);
+    lds_barrier();
+    store_scales();
   }
   // every wave is done with the stage buffers before the epilogue reuses them
   if (Y) lds_barrier();
@@ -500,10 +539,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // They are read back row-contiguous, so 8 consecutive lanes store one whole
   // 128-byte row segment of Y: write misses reach memory as full lines
   // rather than as 16-byte pieces of 32 different rows.
-  constexpr int OUT_ROW = 64 * 2 + 16;               // bytes per staged row (+ pad)
-  static_assert(Cfg::WAVES * WM * OUT_ROW <= STAGES * Cfg::STAGE_BYTES, "output staging fits");
+  constexpr int OUT_ROW = Cfg::OUT_ROW;
   static_assert(TN % 2 == 0, "slices are stored in pairs");
-  int8_t* s_out = stages + wave * (WM * OUT_ROW);
+  int8_t* s_out = lds + Cfg::OUT0 + wave * (WM * OUT_ROW);
   const bool n8 = (N & 7) == 0;
   auto stage_tile = [&](int a, int b, const v16f32& y) {
     uint32_t p[8];
@@ -651,8 +689,8 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
 #ifndef I8MM_LARGE_WAVES_M
 #define I8MM_LARGE_WAVES_M 4
 #endif
-using CfgLarge = GemmCfg<256, 256, 64, 4, I8MM_LARGE_WAVES_M>;
-using CfgSmall = GemmCfg<128, 128, 64, 4>;
+using CfgLarge = GemmCfg<256, 256, 64, 5, I8MM_LARGE_WAVES_M>;
+using CfgSmall = GemmCfg<128, 128, 64, 5>;
 #ifndef I8MM_LARGE_TILE_MIN
 #define I8MM_LARGE_TILE_MIN 256
 #endif
