@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,14 +70,23 @@ def _event_time_ms(fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def _kernel_code_sha256():
+    """SHA-256 of the GEMM kernel's code: its source with comments removed and
+    whitespace collapsed, so that only a change of code (not of its comments)
+    invalidates counters taken on it."""
+    text = open(GEMM_SRC).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def _traffic_from_counters():
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or None
-    when absent or taken on a different version of the kernel source."""
+    when absent or taken on a different version of the kernel code."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
-        src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-        if c.get("kernel_source_sha256") != src_hash:
+        if c.get("kernel_code_sha256") != _kernel_code_sha256():
             return None
         return float(c["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -189,7 +199,7 @@ def _write_counters(pmc_dir):
             "python3 bench.py --write-counters %s" % pmc_dir],
         "counter_note": "FETCH_SIZE and WRITE_SIZE count L2-to-fabric traffic (KiB per dispatch); "
                         "each is scaled by the copy probe's known bytes / its reading",
-        "kernel_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest(),
+        "kernel_code_sha256": _kernel_code_sha256(),
         "fetch_kib_per_dispatch": round(gf, 1), "write_kib_per_dispatch": round(gw, 1),
         "dispatches": [ngf, ngw],
         "copy_probe": {"bytes": COPY_PROBE_BYTES, "fetch_kib": round(cf, 1),

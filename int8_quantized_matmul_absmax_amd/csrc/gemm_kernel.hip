@@ -24,20 +24,23 @@
 // lane -> k assignment, so the sum over k is the same whatever order the
 // instruction uses inside its 32-byte slice (integer sums are exact).
 //
-// Block = 4 wavefronts (one per SIMD) in a 2 x 2 grid over a BN x BM
-// (features x tokens) tile; each wave owns a (BN/2) x (BM/2) sub-tile (4 x 4
-// MFMA tiles for 256 x 256), so each 16-byte LDS fragment read feeds 4 MFMAs.
-// K advances in BK-byte stages through a STAGES-deep ring of LDS buffers
-// filled by direct-to-LDS buffer loads (no register staging); the range check
-// of the buffer descriptors zero-fills rows past M / N and, through an
-// out-of-range offset, chunks past K (and whole stages past the end of K).
+// Block = 8 wavefronts, two per SIMD, in a 2 x 4 grid over a BN x BM
+// (features x tokens) tile; each wave owns a (BN/2) x (BM/4) sub-tile (4 x 2
+// MFMA tiles of 32 x 32 for 256 x 256, 128 accumulator registers), so while
+// one wave of a SIMD waits on LDS or a barrier the other issues MFMAs. Small
+// grids (fewer 256 x 256 tiles than CUs) use 128 x 128 tiles of 4 waves.
+// K advances in BK = 64-byte stages through a ring of five LDS buffers (all
+// of LDS) filled by direct-to-LDS buffer loads (no register staging). Rows
+// past M / N and chunks past K are loaded through an out-of-range offset,
+// which the buffer descriptor turns into zeros.
 //
 // Main loop, step k: wait until stage k+1 has landed, workgroup barrier (stage
-// k+1 visible to every wave; every wave is done reading stage k, whose buffer
-// now takes stage k+STAGES), issue the loads of stage k+STAGES, then the
-// fragment reads of stage k+1 into one register set interleaved with the
-// MFMAs of stage k from the other set, so LDS traffic is spread over the MFMA
-// phase instead of bursting after each barrier.
+// k+1 visible to every wave; every wave is done reading stage k), issue half
+// of the loads of stages k+4 and k+5 (even k) or the other half (odd k), the
+// same rows of both back to back so each operand row is fetched as a whole
+// 128-byte line, then the fragment reads of stage k+1 into one register set
+// interleaved with the MFMAs of stage k from the other set, so LDS traffic is
+// spread over the MFMA phase instead of bursting after each barrier.
 //
 // LDS layout of one stage: rows of BK = 64 bytes (Wq rows first, then Xq
 // rows); 16-byte chunk c of row r sits at position c ^ f(r),
@@ -46,9 +49,10 @@
 // 128-byte (or 256-byte) bank window.
 //
 // Epilogue: per-tile dequantization with the row / column factors staged in
-// LDS; the fp16 outlier product (at most 16 outlier columns: fragments
-// staged at kernel start; more: staged per 16-column step) runs on
-// v_mfma_f32_32x32x16_f16 onto the dequantized tile; lane swaps
+// LDS; the fp16 outlier product (first 16 outlier columns: gathered in the
+// prologue, held in registers through the main loop, then staged in LDS;
+// further columns read per 16-column step) runs on v_mfma_f32_32x32x16_f16
+// onto the dequantized tile; lane swaps
 // (v_permlane32_swap) and a pass through LDS turn each pair of 32-feature
 // slices into whole 128-byte row segments of Y per 8 lanes.
 //
@@ -255,7 +259,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       st16(s_wo + hr * 16 + 8, make_uint4(wpk[4], wpk[5], wpk[6], wpk[7]));
     }
   };
-  // ---- loader: waves 0,1 fill the Wq rows [0, BN), waves 2,3 the Xq rows.
+  // ---- loader: the first half of the waves fill the Wq rows [0, BN), the
+  // second half the Xq rows.
   // Wave-wide load j of wave w fills LDS rows R0 .. R0+RPL-1 of the stage,
   // lane l -> row R0 + l/4, physical chunk l%4, logical chunk (l%4)^f(row).
   const bool loads_w = wave < Cfg::WAVES / 2;
