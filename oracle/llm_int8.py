@@ -45,6 +45,10 @@ Readings taken where the pages are open:
   * the fp16 weight columns of the outlier matmul are recovered from the int8
     weight as fp16(CB * SCB / 127) with SCB broadcast per output row
     ("Usage": recovery of fp16 weights for the outlier matmul);
+  * with the weight kept in fp16 (has_fp16_weights=True, "Usage") the
+    outlier matmul takes the original fp16 columns instead, and the int8
+    codes of W are those of this call's weight (quantized per call, or the
+    caller's codes of the same weight);
   * the outlier set is the union over all rows of one call, listed ascending;
   * sums of the fp16 outlier product and the dequantized result are formed in
     fp64 here (the reference value); the kernel forms them in fp32 and rounds
@@ -284,6 +288,42 @@ def linear_int8_mixed(X16, Wq, sw, threshold=DEFAULT_THRESHOLD, bias=None, rows=
     Y = dequantize_merge(C, sx, sw, Yo, bias)
     return {"cols": cols, "n": int(cols.size), "Xq": Xq, "sx": sx, "C": C,
             "Wo": Wo, "Yo": Yo, "Y": Y}
+
+
+def fp16_weight_columns(W16, cols):
+    """fp16 weight columns for the outlier matmul, from the fp16 weight.
+
+    [HF-blog "Usage"]: has_fp16_weights=True (the default, meant for mixed
+    Int8/FP16 training) keeps the weight in fp16 inside the module, so the
+    outlier matmul takes the weight columns matching the outlier columns of X
+    as they are ([HF-blog "Inside the MatMul"]: the outlier part is an fp16
+    matmul of those columns); no CB * SCB / 127 recovery is involved.
+    Returns W[:, cols] fp16 [N, n].
+    """
+    return _as_f16(W16)[:, np.asarray(cols, np.int64)]
+
+
+def linear_int8_mixed_fp16_weights(X16, W16, threshold=DEFAULT_THRESHOLD, bias=None,
+                                   rows=None, Wq=None, sw=None):
+    """Whole layer with the weight kept in fp16 (has_fp16_weights=True).
+
+    Steps a1-a7 as in `linear_int8_mixed`, with two differences that follow
+    from the module holding W in fp16 ([HF-blog "Usage"]): the int8 normal
+    part uses W quantized per output row at this call (step a4; a caller that
+    still holds the codes of the same W may pass them as Wq, sw), and the
+    outlier part multiplies the original fp16 weight columns.
+    Returns the same dict as `linear_int8_mixed`, plus Wq and sw.
+    """
+    if Wq is None or sw is None:
+        Wq, sw = quantize_weight_rows(W16)
+    cols = detect_outlier_columns(X16, threshold)
+    Xq, sx = quantize_activation_rows(X16, cols, rows)
+    C = int32_accumulators(Xq, Wq)
+    Wo = fp16_weight_columns(W16, cols)
+    Yo = outlier_product(X16, cols, Wo, rows)
+    Y = dequantize_merge(C, sx, sw, Yo, bias)
+    return {"cols": cols, "n": int(cols.size), "Xq": Xq, "sx": sx, "C": C,
+            "Wo": Wo, "Yo": Yo, "Y": Y, "Wq": Wq, "sw": sw}
 
 
 def gelu_erf(x64):

@@ -7,6 +7,10 @@ import pytest
 from oracle import llm_int8 as O
 from tests import test_oracle_pins as P
 
+# the unpatched functions, for mutants built from other oracle steps
+O_ORIG_QUANTIZE = O.quantize_weight_rows
+O_ORIG_RECOVER = O.recover_outlier_weights
+
 
 def _half_away_codes(x_f32, scale_f32):
     prod = np.multiply(np.asarray(x_f32, np.float32), np.asarray(scale_f32, np.float32),
@@ -59,6 +63,11 @@ def _outlier_product_dropped(X16, cols, Wo, rows=None):
     return np.zeros((X.shape[0], np.asarray(Wo).shape[0]))
 
 
+def _fp16_columns_recovered(W16, cols):
+    Wq, sw = O_ORIG_QUANTIZE(W16)
+    return O_ORIG_RECOVER(Wq, sw, cols)
+
+
 def _scale_times_absmax(absmax):
     a = np.asarray(absmax, dtype=np.float32)
     s = np.zeros_like(a)
@@ -76,6 +85,7 @@ MUTANTS = {
     "recovery_wrong_axis": ("recover_outlier_weights", _recover_per_column),
     "outlier_part_dropped": ("outlier_product", _outlier_product_dropped),
     "range_126": ("absmax_scale", _scale_times_absmax),
+    "fp16_mode_uses_recovered_weights": ("fp16_weight_columns", _fp16_columns_recovered),
 }
 
 PINS = [
@@ -90,6 +100,7 @@ PINS = [
     (P.test_planted_columns_are_found_and_scales_below_threshold, ()),
     (P.test_exactly_representable_construction, ()),
     (P.test_threshold_zero_is_fp16_matmul_of_recovered_weights, ()),
+    (P.test_fp16_weights_threshold_zero_is_fp16_matmul_of_original_weights, ()),
 ]
 
 

@@ -393,6 +393,89 @@ def test_error_bound_vs_unquantized(shape):
     assert set(d["planted"].tolist()) <= set(r["cols"].tolist()) or K == 8
 
 
+# ------------------------------------------- weight kept in fp16 (f16 mode)
+
+def test_fp16_weights_threshold_zero_is_fp16_matmul_of_original_weights():
+    """tau = 0 with the weight kept in fp16: every column is an outlier and
+    the layer is the plain matmul of X with the original fp16 W (numpy's
+    float64 matmul). The recovered-weight mode differs from it by the weight
+    rounding error, so this separates the two weight sources."""
+    d = synth.tiny(M=5, K=48, N=7)
+    r = O.linear_int8_mixed_fp16_weights(d["X"], d["W"], 0.0)
+    assert r["n"] == 48 and np.all(r["C"] == 0)
+    ref = d["X"].astype(np.float64) @ d["W"].astype(np.float64).T
+    assert np.allclose(r["Y"], ref, rtol=1e-12, atol=1e-12)
+    Wq, sw = O.quantize_weight_rows(d["W"])
+    rec = O.linear_int8_mixed(d["X"], Wq, sw, 0.0)
+    assert np.max(np.abs(rec["Y"] - ref)) > 1e-6
+
+
+def test_fp16_weights_threshold_infinity_equals_int8_weights_mode():
+    """tau = +inf: no outlier columns, so the weight source of the outlier
+    part never matters and both modes give the same result exactly."""
+    d = synth.tiny(M=6, K=64, N=9)
+    Wq, sw = O.quantize_weight_rows(d["W"])
+    a = O.linear_int8_mixed_fp16_weights(d["X"], d["W"], np.inf)
+    b = O.linear_int8_mixed(d["X"], Wq, sw, np.inf)
+    assert a["n"] == 0
+    assert np.array_equal(a["Y"], b["Y"])
+
+
+def test_fp16_weights_exact_construction_agrees_with_recovery():
+    """W = qw / 64 with every row absmax 127/64: the recovery
+    fp16(q * sw / 127) reproduces W exactly, so with outlier columns present
+    the two modes must agree bit for bit (and the outlier columns taken from
+    W equal the recovered ones)."""
+    rng = np.random.default_rng(11)
+    M, K, N = 6, 64, 10
+    qw = rng.integers(-127, 128, size=(N, K))
+    qw[:, 2] = 127
+    W = (qw / 64.0).astype(np.float16)
+    X = (rng.standard_normal((M, K)) * 0.5).astype(np.float16)
+    X[1, 5] = np.float16(9.0)
+    X[3, 40] = np.float16(-7.25)
+    a = O.linear_int8_mixed_fp16_weights(X, W, 6.0)
+    Wq, sw = O.quantize_weight_rows(W)
+    b = O.linear_int8_mixed(X, Wq, sw, 6.0)
+    assert a["cols"].tolist() == [5, 40]
+    assert np.array_equal(a["Wo"], b["Wo"])
+    assert np.array_equal(a["Y"], b["Y"])
+
+
+@pytest.mark.parametrize("shape", [(4, 8, 8), (16, 256, 256)])
+def test_fp16_weights_error_bound_vs_unquantized(shape):
+    """With the original fp16 weight columns the outlier part carries no
+    weight rounding: the error against X . W^T is bounded by the absmax terms
+    of the normal columns alone (brute force in fp64)."""
+    M, K, N = shape
+    d = synth.tiny(M=M, K=K, N=N)
+    X, W = d["X"], d["W"]
+    if K == 8:
+        X[:, 3] = np.float16(12.5)
+    r = O.linear_int8_mixed_fp16_weights(X, W, 6.0)
+    assert r["n"] > 0
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    Xa = np.abs(X.astype(np.float64))
+    What = r["Wq"].astype(np.float64) * r["sw"].astype(np.float64)[:, None] / 127
+    normal = np.ones(K, bool)
+    normal[r["cols"]] = False
+    for i in range(M):
+        for j in range(N):
+            b = 0.0
+            for k in np.nonzero(normal)[0]:
+                b += Xa[i, k] * float(r["sw"][j]) / 254 + abs(What[j, k]) * float(r["sx"][i]) / 254
+            assert abs(r["Y"][i, j] - exact[i, j]) <= b * (1 + 1e-5) + 1e-12
+
+
+def test_fp16_weights_given_codes_match_per_call_quantization():
+    d = synth.tiny(M=7, K=96, N=12)
+    a = O.linear_int8_mixed_fp16_weights(d["X"], d["W"], 6.0)
+    Wq, sw = O.quantize_weight_rows(d["W"])
+    b = O.linear_int8_mixed_fp16_weights(d["X"], d["W"], 6.0, Wq=Wq, sw=sw)
+    assert np.array_equal(a["Wq"], Wq) and np.array_equal(a["sw"], sw)
+    assert np.array_equal(a["Y"], b["Y"])
+
+
 def test_rows_subset_matches_full():
     d = synth.tiny()
     Wq, sw = O.quantize_weight_rows(d["W"])
