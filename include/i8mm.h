@@ -211,6 +211,43 @@ I8MM_API int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
                       const uint16_t* bias, float threshold, uint16_t* Y,
                       void* workspace, size_t workspace_bytes, i8mm_stream_t stream);
 
+/*
+ * linear_int8_mixed_fp16_weights  (the whole layer for a weight kept in fp16)
+ *
+ * [HF-blog] "Usage": with has_fp16_weights=True (the module's default, meant
+ * for mixed Int8/FP16 training) the layer keeps W in fp16. The steps are
+ * those of linear_int8_mixed, with two differences: the int8 codes of W are
+ * those of this call's W, and the outlier matmul takes the weight columns
+ * from W itself ([HF-blog] "Inside the MatMul": an fp16 matmul of the outlier
+ * columns of X and the matching weight columns), not from CB * SCB / 127.
+ *
+ *   X          fp16 [M, K], read only.
+ *   W          fp16 [N, K] (nn.Linear layout), read only.
+ *   Wq, sw     int8 [N, K], fp32 [N], caller-owned. With quantize_weight != 0
+ *              this call first writes W's per-output-row absmax codes and
+ *              absmaxes into them (as int8_quantize_colwise_weight does);
+ *              with quantize_weight == 0 they must already hold exactly those
+ *              of this W (a caller whose W has not changed since it last
+ *              quantized it skips that pass).
+ *   bias, threshold, Y, workspace
+ *              as in linear_int8_mixed. Given the larger workspace of
+ *              linear_int8_mixed_workspace_bytes_many_outliers(M, K, N), the
+ *              region after the minimal workspace receives the fp16 weight
+ *              columns of the outlier columns, Wo[j, t] = W[j, cols[t]].
+ *
+ *   Y = fp16( C * sx[i] * sw[j] / 127^2 + sum_t X[i, cols[t]] W[j, cols[t]]
+ *             + bias[j] ), sums in fp32.
+ *
+ * M == 0 or N == 0: no work (Wq, sw untouched). All kernels run in order on
+ * `stream` with no host synchronization. Errors: EINVAL, EALIGN, EWORKSPACE,
+ * ERANGE, ENODEVICE, ELAUNCH.
+ */
+I8MM_API int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_t K,
+                      const uint16_t* W, int64_t N, int8_t* Wq, float* sw,
+                      int quantize_weight, const uint16_t* bias, float threshold,
+                      uint16_t* Y, void* workspace, size_t workspace_bytes,
+                      i8mm_stream_t stream);
+
 /* Bytes of workspace linear_int8_mixed needs for M tokens and K features
  * (0 if the sizes are invalid). Host-only, pure. */
 I8MM_API size_t linear_int8_mixed_workspace_bytes(int64_t M, int64_t K);

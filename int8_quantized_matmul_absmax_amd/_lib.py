@@ -22,6 +22,7 @@ EXPORTS = (
     "outlier_detect_gather",
     "int8_mm_dequant",
     "linear_int8_mixed",
+    "linear_int8_mixed_fp16_weights",
     "linear_int8_mixed_workspace_bytes",
     "linear_int8_mixed_workspace_bytes_many_outliers",
     "i8mm_workspace_offsets",
@@ -55,6 +56,8 @@ def _declare(lib):
         "int8_mm_dequant": ([vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "linear_int8_mixed": ([vp, i64, i64, vp, vp, i64, vp, f32, vp, vp, ctypes.c_size_t, vp],
                               i32),
+        "linear_int8_mixed_fp16_weights": ([vp, i64, i64, vp, i64, vp, vp, i32, vp, f32, vp, vp,
+                                            ctypes.c_size_t, vp], i32),
         "linear_int8_mixed_workspace_bytes": ([i64, i64], ctypes.c_size_t),
         "linear_int8_mixed_workspace_bytes_many_outliers": ([i64, i64, i64], ctypes.c_size_t),
         "i8mm_workspace_offsets": ([i64, i64, ctypes.POINTER(ctypes.c_int64)], i32),

@@ -218,15 +218,24 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
   I8MM_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr, s),
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr,
+                        nullptr, s),
       fn));
   return ok();
 }
 
-int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
-                      int64_t N, const uint16_t* bias, float threshold, uint16_t* Y,
-                      void* workspace, size_t workspace_bytes, i8mm_stream_t stream) {
-  const char* fn = "linear_int8_mixed";
+}  // extern "C"
+
+namespace {
+
+// The whole layer after argument checks common to both weight modes. Wf: the
+// fp16 weight when the layer keeps one (its outlier columns feed the outlier
+// product), else nullptr (they are recovered from Wq, sw). quantize_w: write
+// Wf's codes into Wq, sw first.
+int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+              const float* sw, int64_t N, const uint16_t* bias, float threshold, uint16_t* Y,
+              void* workspace, size_t workspace_bytes, hipStream_t s, const uint16_t* Wf,
+              bool quantize_w) {
   I8MM_TRY(check_dims(fn, M, N, K));
   if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
   I8MM_TRY(check_ptr(fn, "X", X, true));
@@ -244,7 +253,6 @@ int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
                 (long long)off[6]);
   if (M == 0 || N == 0) return ok();
   I8MM_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + off[0]);
   int32_t* cols = reinterpret_cast<int32_t*>(ws + off[1]);
@@ -254,19 +262,48 @@ int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
   uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
   const int64_t nwords = (K + 31) / 32;
   const uint32_t tau16 = i8mm::fp16_threshold_pattern(threshold);
+  if (quantize_w)
+    I8MM_TRY(launched(i8mm::launch_rows(Wf, N, K, nullptr, const_cast<int8_t*>(Wq),
+                                        const_cast<float*>(sw), nullptr, nullptr, nullptr, s),
+                      fn));
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
   I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, tau16, bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
-  // With room for it, the recovered outlier weight columns are materialized
-  // for the tiled GEMM (the kernel does nothing for 16 or fewer columns).
+  // With room for it, the fp16 outlier weight columns are materialized for
+  // the tiled GEMM (the kernels do nothing for 16 or fewer columns).
   uint16_t* Wo = nullptr;
   if (!i8mm::gemv_applies(M) && (int64_t)workspace_bytes >= off[6] + wo_region_bytes(N, K)) {
     Wo = reinterpret_cast<uint16_t*>(ws + off[6]);
-    I8MM_TRY(launched(i8mm::launch_recover_outlier_w(Wq, sw, N, K, cols, n_o, Wo, s), fn));
+    if (Wf)
+      I8MM_TRY(launched(i8mm::launch_gather_w_cols(Wf, N, K, cols, n_o, Wo, s), fn));
+    else
+      I8MM_TRY(launched(i8mm::launch_recover_outlier_w(Wq, sw, N, K, cols, n_o, Wo, s), fn));
   }
   I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, Wo, s), fn));
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, Wo, Wf, s), fn));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                      int64_t N, const uint16_t* bias, float threshold, uint16_t* Y,
+                      void* workspace, size_t workspace_bytes, i8mm_stream_t stream) {
+  return run_layer("linear_int8_mixed", X, M, K, Wq, sw, N, bias, threshold, Y, workspace,
+                   workspace_bytes, (hipStream_t)stream, nullptr, false);
+}
+
+int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_t K, const uint16_t* W,
+                                   int64_t N, int8_t* Wq, float* sw, int quantize_weight,
+                                   const uint16_t* bias, float threshold, uint16_t* Y,
+                                   void* workspace, size_t workspace_bytes,
+                                   i8mm_stream_t stream) {
+  const char* fn = "linear_int8_mixed_fp16_weights";
+  I8MM_TRY(check_ptr(fn, "W", W, true));
+  return run_layer(fn, X, M, K, Wq, sw, N, bias, threshold, Y, workspace, workspace_bytes,
+                   (hipStream_t)stream, W, quantize_weight != 0);
 }
 
 int i8mm_gelu_f16(const uint16_t* X, int64_t count, uint16_t* Y, i8mm_stream_t stream) {

@@ -9,12 +9,14 @@
 // Y[i, j] = fp16( C[i, j] * (sx[i] / 127) * (sw[j] / 127)
 //                 + sum_t Xo[i, t] * Wo[j, t] + bias[j] ),
 // C[i, j] = sum_k Xq[i, k] * Wq[j, k]                     (exact int32)
-// Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127))
+// Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)),
+//            or Wf[j, cols[t]] when the fp16 weight Wf is given
 //
 // [Summary] "The full picture" step 3 (Int8 matmul, Int32 result,
 // dequantized by the outer product of the scale vectors) and step 4 (add the
 // 16-bit outlier product); [HF-blog] "Usage" (fp16 weight columns for the
-// outlier matmul recovered as CB * SCB / 127, per output row).
+// outlier matmul recovered as CB * SCB / 127, per output row, when the module
+// holds only the int8 weight; taken from the fp16 weight when it keeps one).
 //
 // Mapping onto the matrix cores. Both operands are K-contiguous (Xq [M, K],
 // Wq [N, K]). v_mfma_i32_32x32x32_i8 takes a 32 x 32-byte slice of each: the
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C,
-    const uint16_t* __restrict__ Wo) {
+    const uint16_t* __restrict__ Wo, const uint16_t* __restrict__ Wf) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN, KS = Cfg::KS;
   constexpr int LOADS = Cfg::LOADS, RPL = Cfg::ROWS_PER_LOAD;
@@ -214,16 +216,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
   // Values held in registers from the prologue to the end of the main loop
   // (the stage buffers fill all of LDS until then), split so that no thread
-  // holds more than nine: thread tid < BM keeps token m0 + tid's factor and
-  // its gathered outlier activations, thread BM + f feature n0 + f's factor,
-  // bias and gathered int8 outlier weight codes (four per register).
+  // holds more than ten: thread tid < BM keeps token m0 + tid's gathered
+  // outlier activations (keep[0..7]) and factor (keep[8]); thread BM + f
+  // keeps feature n0 + f's outlier weights (keep[0..3]: int8 codes, four per
+  // register; keep[0..7] with the weight kept in fp16, Wf given: the fp16
+  // values themselves), factor (keep[8]) and bias (keep[9]).
   static_assert(BM + BN <= Cfg::THREADS, "one held row per thread");
   const bool tok_side = tid < BM;   // uniform per wave
   const int hr = tok_side ? tid : tid - BM;
   const bool h_ok = tok_side ? m0 + hr < M : (hr < BN && n0 + hr < N);
-  uint32_t keep[9];
+  uint32_t keep[10];
 #pragma unroll
-  for (int i = 0; i < 9; ++i) keep[i] = 0;
+  for (int i = 0; i < 10; ++i) keep[i] = 0;
   auto fetch_outliers = [&]() {
     if (!h_ok) return;
     if (tok_side) {
@@ -231,11 +235,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       const uint4 x0 = ld16(src), x1 = ld16(src + 8);
       keep[0] = x0.x; keep[1] = x0.y; keep[2] = x0.z; keep[3] = x0.w;
       keep[4] = x1.x; keep[5] = x1.y; keep[6] = x1.z; keep[7] = x1.w;
+    } else if (Wf) {
+      const uint16_t* row = Wf + (n0 + hr) * K;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        // cols[t] is the same for every lane (a scalar load)
+        const int c = t < n_o ? __builtin_amdgcn_readfirstlane(cols[t]) : 0;
+        const uint32_t h = t < n_o ? (uint32_t)row[c] : 0u;
+        keep[t / 2] |= h << (16 * (t % 2));
+      }
     } else {
       const int8_t* row = Wq + (n0 + hr) * K;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        // cols[t] is the same for every lane (a scalar load)
         const int c = t < n_o ? __builtin_amdgcn_readfirstlane(cols[t]) : 0;
         const uint32_t q = t < n_o ? (uint8_t)row[c] : 0u;
         keep[t / 4] |= q << (8 * (t % 4));
@@ -246,8 +258,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     if (tok_side) {
       st16(s_xo + hr * 16, make_uint4(keep[0], keep[1], keep[2], keep[3]));
       st16(s_xo + hr * 16 + 8, make_uint4(keep[4], keep[5], keep[6], keep[7]));
+    } else if (hr < BN && Wf) {
+      st16(s_wo + hr * 16, make_uint4(keep[0], keep[1], keep[2], keep[3]));
+      st16(s_wo + hr * 16 + 8, make_uint4(keep[4], keep[5], keep[6], keep[7]));
     } else if (hr < BN) {
-      const float swf = __builtin_bit_cast(float, keep[4]);
+      const float swf = __builtin_bit_cast(float, keep[8]);
       uint32_t wpk[8];
 #pragma unroll
       for (int t = 0; t < 16; t += 2) {
@@ -448,8 +463,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     if (tok_side) {
       keep[8] = __builtin_bit_cast(uint32_t, sx[m0 + hr]);
     } else {
-      keep[4] = __builtin_bit_cast(uint32_t, sw[n0 + hr]);
-      if (bias) keep[5] = bias[n0 + hr];
+      keep[8] = __builtin_bit_cast(uint32_t, sw[n0 + hr]);
+      if (bias) keep[9] = bias[n0 + hr];
     }
   }
   // The outlier gathers go after stages 0-1 and before stages 2-3: the first
@@ -463,8 +478,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       if (tok_side) {
         s_ax[hr] = __builtin_bit_cast(float, keep[8]) / 127.0f;
       } else if (hr < BN) {
-        s_fw[hr] = __builtin_bit_cast(float, keep[4]) / 127.0f;
-        s_bias[hr] = h2f((uint16_t)keep[5]);
+        s_fw[hr] = __builtin_bit_cast(float, keep[8]) / 127.0f;
+        s_bias[hr] = h2f((uint16_t)keep[9]);
       }
     }
   };
@@ -599,9 +614,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   };
 
   // Fragments of outlier chunks beyond the first (more than 16 outlier
-  // columns), built straight from global memory: the weight columns are
-  // recovered from Wq as fp16(fl32(fl32(q * sw) / 127)), the activations read
-  // from Xo. Slow, but it keeps the per-slice register footprint small.
+  // columns), built straight from global memory: the weight columns are read
+  // from Wf when the weight is kept in fp16, else recovered from Wq as
+  // fp16(fl32(fl32(q * sw) / 127)); the activations are read from Xo. Slow,
+  // but it keeps the per-slice register footprint small.
   auto wo_frag_g = [&](int a, int t0) -> v8f16 {
     v8f16 w;
     const int64_t f = n0 + wn * WN + a * 32 + l32;
@@ -609,9 +625,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = t0 + lhi * 8 + e;
-      float v = 0.0f;
-      if (t < n_o && f < N) v = ((float)Wq[f * K + cols[t]] * swf) / 127.0f;
-      w[e] = (_Float16)v;
+      if (Wf) {
+        w[e] = (t < n_o && f < N) ? __builtin_bit_cast(_Float16, Wf[f * K + cols[t]])
+                                  : (_Float16)0.0f;
+      } else {
+        float v = 0.0f;
+        if (t < n_o && f < N) v = ((float)Wq[f * K + cols[t]] * swf) / 127.0f;
+        w[e] = (_Float16)v;
+      }
     }
     return w;
   };
@@ -670,23 +691,23 @@ template <class Cfg>
 hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                         const uint16_t* Wo, hipStream_t s) {
+                         const uint16_t* Wo, const uint16_t* Wf, hipStream_t s) {
   const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
   if (C) {
     // parity mode: the epilogue outlier path only
     hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, nullptr);
+                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, nullptr, Wf);
     return hipGetLastError();
   }
   // The outlier count is only known on the device: with Wo given both modes
   // are launched and the one whose case it is not returns at once.
   hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
-                     Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
+                     Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, Wf);
   if (Wo) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s,
-                       Xq, Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo);
+                       Xq, Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, Wf);
   }
   return hipGetLastError();
 }
@@ -706,15 +727,16 @@ constexpr int64_t kLargeTileMin = I8MM_LARGE_TILE_MIN;
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                       const uint16_t* Wo, hipStream_t s) {
+                       const uint16_t* Wo, const uint16_t* Wf, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (gemv_applies(M)) return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, s);
+  if (gemv_applies(M))
+    return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wf, s);
   // 256 x 256 tiles when they give every CU at least one; otherwise the
   // 128 x 128 tiles (four times as many, two blocks per CU).
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_large >= kLargeTileMin)
-    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, s);
-  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, s);
+    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, Wf, s);
+  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, Wf, s);
 }
 
 }  // namespace i8mm

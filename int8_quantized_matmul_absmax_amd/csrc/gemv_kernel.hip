@@ -11,9 +11,11 @@
 // Y[i, j] = fp16( C[i, j] * (sx[i] / 127) * (sw[j] / 127)
 //                 + sum_t Xo[i, t] * Wo[j, t] + bias[j] ),
 // C[i, j] = sum_k Xq[i, k] * Wq[j, k]                     (exact int32)
-// Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127))
+// Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)), or Wf[j, cols[t]]
+// when the fp16 weight Wf is given
 // ([Summary] "The full picture" steps 3-4; [HF-blog] "Usage": outlier weight
-// columns recovered from CB * SCB / 127, per output row.)
+// columns recovered from CB * SCB / 127, per output row, when the module holds
+// only the int8 weight; the fp16 weight's own columns when it keeps one.)
 //
 // One block of 4 wavefronts per 16 output features; the waves split K in
 // 256-byte chunks (chunk c goes to wave c % 4). A chunk is four 64-byte
@@ -64,9 +66,10 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C,
+    const uint16_t* __restrict__ Wf) {
   __shared__ int32_t red[kGvWaves][kGvGroups][16 * 16];
-  __shared__ float s_wo[kGvMaxOut][16];          // recovered outlier weights, [t][j]
+  __shared__ float s_wo[kGvMaxOut][16];          // outlier weights, [t][j]
   __shared__ uint16_t s_xo[kGvMaxTok][kGvMaxOut]; // gathered activations, [m][t]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,7 +133,8 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_i8(
   __builtin_amdgcn_sched_barrier(0);
 
   // Phase 3, outlier part for up to kGvMaxOut columns: the weight bytes
-  // Wq[f0 + j, cols[t]] and the gathered activations Xo[m, t]; they reach LDS
+  // Wq[f0 + j, cols[t]] (or the fp16 weights Wf[f0 + j, cols[t]] when the
+  // layer keeps them) and the gathered activations Xo[m, t]; they reach LDS
   // after the main loop. More columns take the slow path in the epilogue.
   int qv[2] = {0, 0};
   uint4 xv = make_uint4(0, 0, 0, 0);
@@ -138,7 +142,8 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_i8(
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int t = (tid >> 4) + 16 * s2, j = tid & 15;
-      if (t < n_o && j < rows_w) qv[s2] = Wq[(f0 + j) * K + cidx[s2]];
+      if (t < n_o && j < rows_w)
+        qv[s2] = Wf ? (int)Wf[(f0 + j) * K + cidx[s2]] : (int)Wq[(f0 + j) * K + cidx[s2]];
     }
     const int m = tid >> 2;
     if (m < M) xv = ld16(Xo + m * ldo + 8 * (tid & 3));
@@ -186,7 +191,8 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_i8(
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int t = (tid >> 4) + 16 * s2, j = tid & 15;
-      if (t < n_o && j < rows_w) s_wo[t][j] = h2f(f2h(((float)qv[s2] * sw[f0 + j]) / 127.0f));
+      if (t < n_o && j < rows_w)
+        s_wo[t][j] = Wf ? h2f((uint32_t)qv[s2]) : h2f(f2h(((float)qv[s2] * sw[f0 + j]) / 127.0f));
     }
     const int m = tid >> 2;
     if (m < M) st16(&s_xo[m][8 * (tid & 3)], xv);
@@ -213,7 +219,8 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_i8(
       for (int t = 0; t < n_o; ++t) yo += h2f(s_xo[m][t]) * s_wo[t][jf];
     } else {
       for (int t = 0; t < n_o; ++t) {
-        const float wo = h2f(f2h(((float)Wq[f * K + cols[t]] * swf) / 127.0f));
+        const float wo = Wf ? h2f(Wf[f * K + cols[t]])
+                            : h2f(f2h(((float)Wq[f * K + cols[t]] * swf) / 127.0f));
         yo += h2f(Xo[m * ldo + t]) * wo;
       }
     }
@@ -228,15 +235,15 @@ bool gemv_applies(int64_t M) { return M > 0 && M <= kGvMaxTok; }
 hipError_t launch_gemv(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                       hipStream_t s) {
+                       const uint16_t* Wf, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((N + kGvFeat - 1) / kGvFeat);
   if (C)
     hipLaunchKernelGGL(k_gemv_i8<true>, dim3(blocks), dim3(kGvThreads), 0, s, Xq, Wq, sx, sw,
-                       (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
+                       (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wf);
   else
     hipLaunchKernelGGL(k_gemv_i8<false>, dim3(blocks), dim3(kGvThreads), 0, s, Xq, Wq, sx, sw,
-                       (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C);
+                       (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wf);
   return hipGetLastError();
 }
 

@@ -28,13 +28,17 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* 
                        int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                        hipStream_t s);
 
-// Wo: the recovered fp16 outlier weight columns [N, LD(n)] written by
-// launch_recover_outlier_w, or nullptr; with more than 16 outlier columns and
-// Wo given, the outlier product runs as a second main-loop segment.
+// Wo: the fp16 outlier weight columns [N, LD(n)] written by
+// launch_recover_outlier_w (or launch_gather_w_cols), or nullptr; with more
+// than 16 outlier columns and Wo given, the outlier product runs as a second
+// main-loop segment. Wf: the fp16 weight [N, K] when the layer keeps one
+// (its columns are the outlier weights), or nullptr (they are recovered from
+// Wq and sw).
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
                        const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
-                       uint16_t* Y, int32_t* C, const uint16_t* Wo, hipStream_t s);
+                       uint16_t* Y, int32_t* C, const uint16_t* Wo, const uint16_t* Wf,
+                       hipStream_t s);
 
 // Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)) for t < n, +0.0 up
 // to LD(n); nothing when n <= 16 (n read on the device).
@@ -42,13 +46,18 @@ hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N
                                     const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
                                     hipStream_t s);
 
+// Wo[j, t] = Wf[j, cols[t]] (the fp16 weight's own columns) for t < n, +0.0
+// up to LD(n); nothing when n <= 16 (n read on the device).
+hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
+                                const int32_t* n_out, uint16_t* Wo, hipStream_t s);
+
 // Few-token form of launch_gemm (same arguments and results), used for
 // 1 <= M <= 64.
 bool gemv_applies(int64_t M);
 hipError_t launch_gemv(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
                        const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
-                       uint16_t* Y, int32_t* C, hipStream_t s);
+                       uint16_t* Y, int32_t* C, const uint16_t* Wf, hipStream_t s);
 
 hipError_t launch_gelu(const uint16_t* X, int64_t count, uint16_t* Y, hipStream_t s);
 

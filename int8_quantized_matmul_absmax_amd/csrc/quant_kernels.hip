@@ -394,6 +394,32 @@ __global__ __launch_bounds__(256) void k_recover_outlier_w(
   }
 }
 
+// Outlier weight columns of a layer that keeps its weight in fp16 ([HF-blog]
+// "Usage", has_fp16_weights=True): Wo[j, t] = W[j, cols[t]] as they are, for
+// t < n, +0.0 up to LD(n), 8 columns per thread over the same (row, column
+// chunk) tasks as the recovery above. Nothing when n <= 16 (the GEMM stages
+// those itself).
+__global__ __launch_bounds__(256) void k_gather_w_cols(const uint16_t* __restrict__ W, int64_t N,
+                                                      int64_t K, const int32_t* __restrict__ cols,
+                                                      const int32_t* __restrict__ n_out,
+                                                      uint16_t* __restrict__ Wo) {
+  const int n = *n_out;
+  if (n <= 16) return;
+  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
+  const int64_t chunks = (ld + kRecoverCols - 1) / kRecoverCols;
+  for (int64_t task = blockIdx.x; task < N * chunks; task += gridDim.x) {
+    const int64_t j = task / chunks;
+    const int64_t t0 = (task - j * chunks) * kRecoverCols + (int64_t)threadIdx.x * 8;
+    if (t0 >= ld) continue;
+    const uint16_t* row = W + j * K;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = t0 + e < n ? (uint32_t)row[cols[t0 + e]] : 0u;
+    st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                      h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
+  }
+}
+
 // Exact-erf GELU in fp32 (activation between the two layers of an MLP block).
 __global__ void k_gelu(const uint16_t* __restrict__ X, int64_t count, uint16_t* __restrict__ Y) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -495,6 +521,16 @@ hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N
   const int64_t blocks = std::min<int64_t>(max_tasks, 2048);
   hipLaunchKernelGGL(k_recover_outlier_w, dim3((unsigned)blocks), dim3(256), 0, s, Wq, sw, N, K,
                      cols, n_out, Wo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
+                                const int32_t* n_out, uint16_t* Wo, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int64_t max_tasks = N * ((I8MM_OUTLIER_LD(K) + kRecoverCols - 1) / kRecoverCols);
+  const int64_t blocks = std::min<int64_t>(max_tasks, 2048);
+  hipLaunchKernelGGL(k_gather_w_cols, dim3((unsigned)blocks), dim3(256), 0, s, Wf, N, K, cols,
+                     n_out, Wo);
   return hipGetLastError();
 }
 

@@ -183,6 +183,39 @@ def linear_int8_mixed(X, Wq, sw, bias=None, threshold=DEFAULT_THRESHOLD, workspa
     return Y.reshape(*lead, N)
 
 
+def linear_int8_mixed_fp16_weights(X, W, Wq, sw, quantize_weight=True, bias=None,
+                                   threshold=DEFAULT_THRESHOLD, workspace=None, out=None):
+    """The whole layer for a weight kept in fp16 (has_fp16_weights=True).
+    W [N, K] fp16; Wq [N, K] int8 and sw [N] fp32 are caller-owned buffers that
+    receive W's codes when quantize_weight (else they must already hold them).
+    The outlier product uses W's own columns. X [..., K] fp16 -> Y [..., N]."""
+    lib = _lib.load_library()
+    _need(X, "X", torch.float16)
+    _need(W, "W", torch.float16, 2)
+    _need(Wq, "Wq", torch.int8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    lead = X.shape[:-1]
+    X2 = _flatten_tokens(X)
+    M, K = X2.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(Wq.shape) != (N, K) or sw.numel() != N:
+        raise ValueError("shape mismatch")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+    dev = X.device
+    if workspace is None:
+        need = workspace_bytes(M, K, N)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    _need(Y, "out", torch.float16)
+    _lib.check(lib.linear_int8_mixed_fp16_weights(
+        _ptr(X2), M, K, _ptr(W), N, _ptr(Wq), _ptr(sw), 1 if quantize_weight else 0, _ptr(bias),
+        float(threshold), _ptr(Y), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return Y.reshape(*lead, N)
+
+
 def gelu_f16(X, out=None):
     """Exact-erf GELU in fp32 on an fp16 tensor (glue between MLP layers)."""
     lib = _lib.load_library()

@@ -151,6 +151,36 @@ def test_validation_linear(lib):
     assert f(*bad) == _lib.I8MM_OK
 
 
+def test_validation_linear_fp16_weights(lib):
+    """The fp16-weight layer call: the weight W is required and aligned, the
+    rest is validated as in linear_int8_mixed, all before any launch."""
+    f = lib.linear_int8_mixed_fp16_weights
+    M, K, N = 8, 64, 32
+    need = lib.linear_int8_mixed_workspace_bytes(M, K)
+    ws = ctypes.c_void_p(0x100000)
+    args = [A, M, K, A2, N, A, A2, 1, NUL, 6.0, A2, ws, need, NUL]
+    bad = list(args); bad[3] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[3] = MIS
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(args); bad[5] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[6] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[12] = need - 1
+    assert f(*bad) == _lib.I8MM_EWORKSPACE
+    bad = list(args); bad[9] = math.nan
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[10] = NUL
+    assert f(*bad) == _lib.I8MM_EINVAL
+    bad = list(args); bad[2] = K + 8
+    assert f(*bad) == _lib.I8MM_EALIGN
+    bad = list(args); bad[2] = (_lib.I8MM_MAX_K // 16 + 1) * 16
+    assert f(*bad) == _lib.I8MM_ERANGE
+    bad = list(args); bad[1] = 0; bad[12] = lib.linear_int8_mixed_workspace_bytes(0, K)
+    assert f(*bad) == _lib.I8MM_OK
+
+
 def test_validation_gelu(lib):
     assert lib.i8mm_gelu_f16(A, -1, A, NUL) == _lib.I8MM_EINVAL
     assert lib.i8mm_gelu_f16(MIS, 4, A, NUL) == _lib.I8MM_EALIGN
