@@ -399,6 +399,28 @@ def _sweep():
               "eff_tops_layer2": round(fl / (t2 * 1e-6) / 1e12, 1), "timing": "hip events"})
         del Wq1, Wq2, ws1, ws2, Y1, G, Y2, X
 
+    # the weight kept in fp16 (has_fp16_weights=True), OPT-6.7B FFN up shape:
+    # W quantized at every call, and with the codes of an unchanged W given
+    d = synth.opt_ffn_up()
+    X = torch.from_numpy(d["X"]).cuda()
+    W = torch.from_numpy(d["W"]).cuda()
+    M, K = d["X"].shape
+    N = W.shape[0]
+    del d
+    Wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sw = torch.empty((N,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    tq = ev_us(lambda: ops.linear_int8_mixed_fp16_weights(X, W, Wq, sw, True, None, 6.0, ws, Y), 20)
+    tc = ev_us(lambda: ops.linear_int8_mixed_fp16_weights(X, W, Wq, sw, False, None, 6.0, ws, Y), 20)
+    fl = 2.0 * M * N * K
+    emit({"case": "fp16 weights, OPT FFN up", "M": M, "K": K, "N": N,
+          "us_weight_quantized_at_call": round(tq, 1), "us_codes_given": round(tc, 1),
+          "eff_tops_quantized_at_call": round(fl / (tq * 1e-6) / 1e12, 1),
+          "eff_tops_codes_given": round(fl / (tc * 1e-6) / 1e12, 1),
+          "timing": "hip events, same buffers each call"})
+    del X, W, Wq, sw, ws, Y
+
     # 175B-scale FFN layer
     d = synth.ffn_175b()
     X = torch.from_numpy(d["X"]).cuda()
