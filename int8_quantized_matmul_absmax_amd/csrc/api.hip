@@ -266,6 +266,13 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
     I8MM_TRY(launched(i8mm::launch_rows(Wf, N, K, nullptr, const_cast<int8_t*>(Wq),
                                         const_cast<float*>(sw), nullptr, nullptr, nullptr, s),
                       fn));
+  if (i8mm::decode_applies(M, K)) {
+    // few tokens: the whole layer in one launch
+    I8MM_TRY(launched(i8mm::launch_decode(X, Wq, sw, M, N, K, tau16, bias, Y, Wf, bitmap, cols,
+                                          n_o, sx, Xq, Xo, s),
+                      fn));
+    return ok();
+  }
   I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
   I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, tau16, bitmap, s), fn));
   I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));

@@ -51,6 +51,17 @@ hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N
 hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
                                 const int32_t* n_out, uint16_t* Wo, hipStream_t s);
 
+// The whole layer in one launch for 1 <= M <= 16 tokens whose codes fit in
+// LDS (decode_applies): detection, row quantization and the few-token
+// matmul with its epilogue. Writes the same intermediates as the separate
+// kernels (bitmap, cols, n, sx, Xq, Xo with leading dimension LD(n)) and Y.
+// Wf: the fp16 weight when the layer keeps one, else nullptr.
+bool decode_applies(int64_t M, int64_t K);
+hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, int64_t M,
+                         int64_t N, int64_t K, uint32_t tau16, const uint16_t* bias, uint16_t* Y,
+                         const uint16_t* Wf, uint32_t* bitmap, int32_t* cols, int32_t* n_out,
+                         float* sx, int8_t* Xq, uint16_t* Xo, hipStream_t s);
+
 // Few-token form of launch_gemm (same arguments and results), used for
 // 1 <= M <= 64.
 bool gemv_applies(int64_t M);

@@ -100,50 +100,6 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
   }
 }
 
-// Exclusive prefix of popcount over the bitmap words, in LDS. Returns the
-// total (the outlier count n). All threads of the block must call it.
-__device__ int bitmap_prefix(const uint32_t* sbm, uint32_t* spre, int nwords, int* sred) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (nwords + kRowThreads - 1) / kRowThreads;
-  const int w0 = tid * per;
-  const int w1 = min(nwords, w0 + per);
-  int local = 0;
-  for (int w = w0; w < w1; ++w) local += __popc(sbm[w]);
-  int incl = wave_inclusive_scan(local, lane);
-  if (lane == 63) sred[wave] = incl;
-  __syncthreads();
-  int wave_off = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < kRowThreads / kWave; ++i) {
-    wave_off += i < wave ? sred[i] : 0;
-    total += sred[i];
-  }
-  int run = wave_off + incl - local;
-  for (int w = w0; w < w1; ++w) {
-    spre[w] = (uint32_t)run;
-    run += __popc(sbm[w]);
-  }
-  __syncthreads();
-  return total;
-}
-
-// Writes cols[p] = k for the p-th set bit k (ascending) and *n_out.
-__device__ void write_cols(const uint32_t* sbm, const uint32_t* spre, int nwords, int n,
-                           int32_t* __restrict__ cols, int32_t* __restrict__ n_out) {
-  if (cols) {
-    for (int w = threadIdx.x; w < nwords; w += kRowThreads) {
-      uint32_t bits = sbm[w];
-      int p = (int)spre[w];
-      while (bits) {
-        int b = __builtin_ctz(bits);
-        cols[p++] = w * 32 + b;
-        bits &= bits - 1;
-      }
-    }
-  }
-  if (n_out && threadIdx.x == 0) *n_out = n;
-}
-
 __global__ __launch_bounds__(256) void k_cols_from_bitmap(const uint32_t* __restrict__ bitmap,
                                                           int64_t K, int32_t* __restrict__ cols,
                                                           int32_t* __restrict__ n_out) {
@@ -265,26 +221,7 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
       m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
     return m;
   };
-  // Codes of 8 elements: y = fl32(x * s); y + 1.5 * 2^23 rounds to the nearest
-  // integer with ties to even (the addend is even and |y| <= 127 < 2^22), so
-  // the low byte of its bit pattern is the two's complement code rne(y). No
-  // clamp is needed: s = fl32(127 / a) and abs(x) <= a give abs(y) <= 127 up
-  // to one rounding, and rne of that is within [-127, 127].
-  auto codes8 = [&](const uint4& t, float s) -> uint2 {
-    const float magic = 12582912.0f;
-    uint32_t r[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float y = h2f(half_of(t, e)) * s;
-      r[e] = __builtin_bit_cast(uint32_t, y + magic);
-    }
-    const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
-    return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                      __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
-  };
+  auto codes8 = [](const uint4& t, float s) -> uint2 { return codes8_rne(t, s); };
 
   for (int64_t row = row_lo + wave; row < row_hi; row += kRowThreads / kWave) {
     const uint16_t* xr = X + row * K;
