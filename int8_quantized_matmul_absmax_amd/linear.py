@@ -11,11 +11,64 @@ Multiplication for transformers at scale ...", section "Usage":
 * has_fp16_weights=True (the default of the pages' module, meant for mixed
   Int8/FP16 training): the module keeps W in fp16; its int8 codes are those of
   the current W, and the outlier matmul uses W's own fp16 columns.
+
+The quantized pair can be saved and loaded again without re-quantizing
+(section "Saving 8-bit state dicts on the Hub" names the missing piece: the
+CB and SCB statistics were not kept in the state dict): as a safetensors file
+holding CB and SCB under those names, and through the module's state dict,
+whose extra state records that the buffers hold a quantized weight.
 """
 
 import torch
 
 from . import ops
+
+INT8_FORMAT = "llm-int8/per-output-row-absmax/v1"
+
+
+def save_int8_weight(path, Wq, sw, bias=None, threshold=ops.DEFAULT_THRESHOLD):
+    """Write the quantized weight pair to a safetensors file: CB = Wq (int8
+    [out, in], the codes), SCB = sw (fp32 [out], the per-output-row absmax),
+    optional bias (fp16 [out]); the threshold and the shape go in the
+    metadata. Tensors may live on any device."""
+    from safetensors.torch import save_file
+    if Wq.dtype != torch.int8 or Wq.dim() != 2:
+        raise TypeError("Wq must be an int8 [out, in] tensor")
+    N, K = Wq.shape
+    if sw.dtype != torch.float32 or tuple(sw.shape) != (N,):
+        raise TypeError("sw must be a float32 [out] tensor")
+    tensors = {"CB": Wq.detach().cpu().contiguous(), "SCB": sw.detach().cpu().contiguous()}
+    if bias is not None:
+        if tuple(bias.shape) != (N,):
+            raise ValueError("bias must be [out]")
+        tensors["bias"] = bias.detach().to(torch.float16).cpu().contiguous()
+    meta = {"format": INT8_FORMAT, "threshold": repr(float(threshold)),
+            "out_features": str(N), "in_features": str(K)}
+    save_file(tensors, path, metadata=meta)
+
+
+def load_int8_weight(path):
+    """Read a file written by save_int8_weight (safetensors: no code is run).
+    Returns {"CB", "SCB", "bias" (or None), "threshold"} with CPU tensors;
+    raises ValueError on a different format or inconsistent tensors."""
+    from safetensors import safe_open
+    with safe_open(path, framework="pt") as f:
+        meta = f.metadata() or {}
+        if meta.get("format") != INT8_FORMAT:
+            raise ValueError("not an int8 weight file of format %s" % INT8_FORMAT)
+        keys = set(f.keys())
+        if not {"CB", "SCB"} <= keys or not keys <= {"CB", "SCB", "bias"}:
+            raise ValueError("unexpected tensors %s" % sorted(keys))
+        CB, SCB = f.get_tensor("CB"), f.get_tensor("SCB")
+        bias = f.get_tensor("bias") if "bias" in keys else None
+    N, K = int(meta["out_features"]), int(meta["in_features"])
+    if CB.dtype != torch.int8 or tuple(CB.shape) != (N, K):
+        raise ValueError("CB must be int8 [%d, %d]" % (N, K))
+    if SCB.dtype != torch.float32 or tuple(SCB.shape) != (N,):
+        raise ValueError("SCB must be float32 [%d]" % N)
+    if bias is not None and (bias.dtype != torch.float16 or tuple(bias.shape) != (N,)):
+        raise ValueError("bias must be float16 [%d]" % N)
+    return {"CB": CB, "SCB": SCB, "bias": bias, "threshold": float(meta["threshold"])}
 
 
 class Int8Linear(torch.nn.Module):
@@ -35,8 +88,8 @@ class Int8Linear(torch.nn.Module):
         self.register_buffer("weight", torch.zeros((out_features, in_features),
                                                    dtype=torch.float16, device=device)
                              if self.has_fp16_weights else None)
-        self.bias = (torch.zeros((out_features,), dtype=torch.float16, device=device)
-                     if bias else None)
+        self.register_buffer("bias", torch.zeros((out_features,), dtype=torch.float16,
+                                                 device=device) if bias else None)
         # fp16-weight mode: re-quantize W at every call (its codes follow W
         # as it changes); set False to re-quantize only after set_weight_.
         self.requantize_every_call = True
@@ -112,6 +165,44 @@ class Int8Linear(torch.nn.Module):
         if M > 0:
             self._codes_current = True
         return Y
+
+    # ---- saving and loading the quantized pair
+    def save_int8(self, path):
+        """Write CB, SCB (and bias) to a safetensors file (int8 mode, quantized)."""
+        if self.has_fp16_weights:
+            raise RuntimeError("has_fp16_weights=True keeps the fp16 weight; save its state_dict")
+        if not self._quantized:
+            raise RuntimeError("nothing to save: the weight is not quantized")
+        save_int8_weight(path, self.Wq, self.sw, self.bias, self.threshold)
+
+    @classmethod
+    def from_int8_file(cls, path, device="cuda"):
+        """A quantized int8-mode module from a save_int8 file (no re-quantization)."""
+        d = load_int8_weight(path)
+        N, K = d["CB"].shape
+        m = cls(K, N, bias=d["bias"] is not None, threshold=d["threshold"], device=device)
+        with torch.no_grad():
+            m.Wq.copy_(d["CB"])
+            m.sw.copy_(d["SCB"])
+            if d["bias"] is not None:
+                m.bias.copy_(d["bias"])
+        m._quantized = True
+        return m
+
+    def get_extra_state(self):
+        # the buffers alone cannot tell a quantized weight from the zeros of a
+        # fresh module
+        return {"format": INT8_FORMAT, "quantized": bool(self._quantized),
+                "has_fp16_weights": self.has_fp16_weights, "threshold": self.threshold}
+
+    def set_extra_state(self, state):
+        if state.get("format") != INT8_FORMAT:
+            raise ValueError("state of a different format")
+        if bool(state["has_fp16_weights"]) != self.has_fp16_weights:
+            raise ValueError("state of the other weight mode")
+        self.threshold = float(state["threshold"])
+        self._quantized = bool(state["quantized"])
+        self._codes_current = False
 
     def extra_repr(self):
         return "in_features=%d, out_features=%d, threshold=%g, has_fp16_weights=%s, ready=%s" % (

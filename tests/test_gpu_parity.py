@@ -440,3 +440,31 @@ def test_gelu(gpu):
     # within one fp16 ulp of the correctly rounded fp64 value
     ulp = np.spacing(np.abs(ref16)).astype(np.float64)
     assert np.all(np.abs(Y.astype(np.float64) - ref16.astype(np.float64)) <= ulp + 1e-12)
+
+
+def test_int8_linear_save_load(gpu, tmp_path):
+    """The quantized pair saved and loaded (file and state dict) gives the
+    same module: same codes, same output bits, and no second quantization."""
+    note("Int8Linear save/load")
+    rng = np.random.default_rng(77)
+    W = synth.normal_f16(rng, (96, 256), 0.05)
+    b = synth.normal_f16(rng, (96,), 0.5)
+    X = synth.normal_f16(rng, (40, 256), 1.0)
+    X[:, 7] = 12.0
+    lin = gpu.Int8Linear(256, 96, bias=True)
+    lin.quantize_(dev(W), dev(b))
+    Y0 = host(lin(dev(X)))
+    p = str(tmp_path / "lin.safetensors")
+    lin.save_int8(p)
+    lin2 = gpu.Int8Linear.from_int8_file(p)
+    assert lin2.quantized
+    assert np.array_equal(host(lin2.CB), host(lin.CB))
+    assert np.array_equal(host(lin2(dev(X))).view(np.uint16), Y0.view(np.uint16))
+    with pytest.raises(RuntimeError):
+        lin2.quantize_(dev(W))
+    sd = str(tmp_path / "lin.pt")
+    torch.save(lin.state_dict(), sd)
+    lin3 = gpu.Int8Linear(256, 96, bias=True)
+    lin3.load_state_dict(torch.load(sd, weights_only=True))
+    assert lin3.quantized
+    assert np.array_equal(host(lin3(dev(X))).view(np.uint16), Y0.view(np.uint16))
