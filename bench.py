@@ -93,13 +93,19 @@ def _traffic_from_counters():
         return None
 
 
-def _cpu_baseline(d, Wq_ref, sw_ref, M, N, K, target_s):
+def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y):
     """The oracle as it stands, on a bounded sample of rows: outlier detection
     over all rows, then quantization, int32 GEMM, outlier product and
     dequantization for S sampled rows x all N outputs. Scaled to TOPS by the
-    dense-equivalent 2*S*N*K."""
+    dense-equivalent 2*S*N*K. The same leg checks the timed GPU output against
+    the oracle on the rows rows_y (Y_rows, host copy) and the GPU weight codes
+    (Wq_gpu, host copy) bit for bit."""
     import numpy as np
     from oracle import llm_int8 as O
+    Wq_ref, sw_ref = O.quantize_weight_rows(d["W"])
+    ref = O.linear_int8_mixed(d["X"], Wq_ref, sw_ref, 6.0, rows=rows_y)
+    parity = {"y_max_abs_rel_err_sampled_rows": O.max_abs_rel_error(Y_rows, ref["Y"]),
+              "weight_codes_bitexact": bool(np.array_equal(Wq_gpu, Wq_ref))}
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -125,9 +131,9 @@ def _cpu_baseline(d, Wq_ref, sw_ref, M, N, K, target_s):
         calls += 1
     dt = total / calls
     tops = 2.0 * rows.size * N * K / dt / 1e12
-    return {"value": round(tops, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of %d token rows x all %d outputs (outlier detection over all rows), "
-                      "%d call(s), %.2f s each" % (rows.size, M, N, calls, dt)}
+    return ({"value": round(tops, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+             "sample": "%d of %d token rows x all %d outputs (outlier detection over all rows), "
+                       "%d call(s), %.2f s each" % (rows.size, M, N, calls, dt)}, parity)
 
 
 COPY_PROBE_BYTES = 512 << 20
@@ -494,7 +500,6 @@ def main():
     import torch
 
     import int8_quantized_matmul_absmax_amd as i8
-    from oracle import llm_int8 as O
 
     i8.ensure_built()
     ops = i8.ops
@@ -575,17 +580,14 @@ def main():
     ms_rowq = _event_time_ms(rowq, args.steps, stream)
     rowq_gbps = (3.0 * M * K + 4.0 * M) / (ms_rowq * 1e-3) / 1e9
 
-    # ---- parity spot check of the timed output (sampled rows vs the oracle)
-    Wq_ref, sw_ref = O.quantize_weight_rows(W_h)
-    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(1).choice(M, 8)]))
-    ref = O.linear_int8_mixed(X_h, Wq_ref, sw_ref, 6.0, rows=rows)
-    Y_last = pool[(args.steps - 1) % n_sets]["Y"]
-    err = O.max_abs_rel_error(Y_last[torch.from_numpy(rows).cuda()].cpu().numpy(), ref["Y"])
-    codes_ok = bool(np.array_equal(Wq0.cpu().numpy(), Wq_ref))
-
-    cpu = None
+    # ---- CPU baseline (the oracle timed on the host), which also checks the
+    # timed output on sampled rows and the weight codes against the oracle
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(d, Wq_ref, sw_ref, M, N, K, args.cpu_seconds)
+        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(1).choice(M, 8)]))
+        Y_last = pool[(args.steps - 1) % n_sets]["Y"]
+        cpu, parity = _cpu_baseline(d, M, N, K, args.cpu_seconds, Wq0.cpu().numpy(),
+                                    Y_last[torch.from_numpy(rows).cuda()].cpu().numpy(), rows)
 
     traffic = _traffic_from_counters() if args.workload == "opt6.7b_ffn_up" else None
     out = {
@@ -616,7 +618,7 @@ def main():
                      "weight_once_gbps": round(wq_gbps, 1),
                      "weight_once_hbm_frac": round(wq_gbps / PEAK_HBM_GBPS, 4),
                      "weight_once_ms": round(t_wq, 6)},
-        "parity": {"y_max_abs_rel_err_sampled_rows": err, "weight_codes_bitexact": codes_ok},
+        "parity": parity,
         "cpu_baseline": cpu,
         "rotation_sets": n_sets,
         "timed_wall_s": round(wall, 4),
