@@ -592,7 +592,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       if (tok < M) {
         uint16_t* dst = Y + tok * N + f;
         if (n8 && f + 7 < N) {
-          st16(dst, v);
+          // streaming store: Y is written once and not read back by this
+          // kernel, so it should not displace operand lines in the caches
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
