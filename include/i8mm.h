@@ -268,7 +268,10 @@ I8MM_API size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64
 /* Byte offsets inside the workspace, host-only and pure. Writes, in order:
  * offsets[0] bitmap (uint32 [ceil(K/32)]), [1] cols (int32 [K]),
  * [2] n (int32 [1]), [3] sx (fp32 [M]), [4] Xq (int8 [M, K]),
- * [5] Xo (fp16 [M, I8MM_OUTLIER_LD(K)] capacity), [6] total bytes.
+ * [5] Xo (fp16 [M, I8MM_OUTLIER_LD(K)] capacity), [6] total bytes. Between
+ * the end of Xo and the total lies scratch of the detection (per-row-band
+ * partial flag words, 16 x ceil(K/32) uint32 at most), whose contents on
+ * entry do not matter.
  * `offsets` is a host array of 7 int64. Errors: EINVAL. */
 I8MM_API int i8mm_workspace_offsets(int64_t M, int64_t K, int64_t* offsets);
 

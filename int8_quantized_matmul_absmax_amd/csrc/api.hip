@@ -84,8 +84,9 @@ int check_ptr(const char* fn, const char* name, const void* p, bool required) {
 constexpr int64_t kAlign = 256;
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Workspace of linear_int8_mixed: bitmap | cols | n | sx | Xq | Xo.
-bool layout(int64_t M, int64_t K, int64_t* off) {
+// Workspace of linear_int8_mixed: bitmap | cols | n | sx | Xq | Xo |
+// partial flag words (kMaxFlagBands x ceil(K/32), at *part when given).
+bool layout(int64_t M, int64_t K, int64_t* off, int64_t* part = nullptr) {
   if (M < 0 || K < 0 || K % 16 != 0 || K > I8MM_MAX_K || M > INT32_MAX) return false;
   int64_t p = 0;
   off[0] = p; p = round_up(p + (K + 31) / 32 * 4, kAlign);
@@ -94,6 +95,8 @@ bool layout(int64_t M, int64_t K, int64_t* off) {
   off[3] = p; p = round_up(p + M * 4, kAlign);
   off[4] = p; p = round_up(p + M * K, kAlign);
   off[5] = p; p = round_up(p + M * I8MM_OUTLIER_LD(K) * 2, kAlign);
+  if (part) *part = p;
+  p = round_up(p + i8mm::kMaxFlagBands * ((K + 31) / 32) * 4, kAlign);
   off[6] = p;
   return true;
 }
@@ -243,8 +246,8 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
   I8MM_TRY(check_ptr(fn, "sw", sw, true));
   I8MM_TRY(check_ptr(fn, "bias", bias, false));
   I8MM_TRY(check_ptr(fn, "Y", Y, true));
-  int64_t off[7];
-  layout(M, K, off);
+  int64_t off[7], off_part = 0;
+  layout(M, K, off, &off_part);
   if (!workspace) return fail(I8MM_EWORKSPACE, "%s: workspace is NULL", fn);
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
     return fail(I8MM_EALIGN, "%s: workspace is not 256-byte aligned", fn);
@@ -260,7 +263,6 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
   float* sx = reinterpret_cast<float*>(ws + off[3]);
   int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
   uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
-  const int64_t nwords = (K + 31) / 32;
   const uint32_t tau16 = i8mm::fp16_threshold_pattern(threshold);
   if (quantize_w)
     I8MM_TRY(launched(i8mm::launch_rows(Wf, N, K, nullptr, const_cast<int8_t*>(Wq),
@@ -273,9 +275,13 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
                       fn));
     return ok();
   }
-  I8MM_TRY(launched(i8mm::launch_fill_u32(bitmap, nwords, 0u, s), fn));
-  I8MM_TRY(launched(i8mm::launch_outlier_flags(X, M, K, tau16, bitmap, s), fn));
-  I8MM_TRY(launched(i8mm::launch_rows(X, M, K, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+  // detection as per-band partial flags (no clearing launch), then the row
+  // pass, which ORs them and also writes the bitmap, cols and n
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + off_part);
+  const int bands = i8mm::flag_bands(M, K);
+  I8MM_TRY(launched(i8mm::launch_outlier_flag_bands(X, M, K, tau16, bands, part, s), fn));
+  I8MM_TRY(launched(
+      i8mm::launch_rows_banded(X, M, K, part, bands, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
   // With room for it, the fp16 outlier weight columns are materialized for
   // the tiled GEMM (the kernels do nothing for 16 or fewer columns).
   uint16_t* Wo = nullptr;

@@ -99,11 +99,31 @@ __device__ __forceinline__ uint2 codes8_rne(const uint4& t, float s) {
                     __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
 }
 
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// operations complete (lgkmcnt(0), gfx9 encoding), then s_barrier. Global
+// loads stay in flight across it; __syncthreads' fence would wait for them.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_only_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool kLdsOnly>
+__device__ __forceinline__ void block_sync() {
+  if constexpr (kLdsOnly) lds_only_barrier();
+  else __syncthreads();
+}
+
 // Outlier bitmap helpers for blocks of kBlockThreads threads.
 constexpr int kBlockThreads = 256;
 
 // Exclusive prefix of popcount over the bitmap words, in LDS. Returns the
 // total (the outlier count n). All threads of the block must call it.
+// kLdsOnly: its barriers leave the caller's global loads in flight.
+template <bool kLdsOnly = false>
 __device__ inline int bitmap_prefix(const uint32_t* sbm, uint32_t* spre, int nwords, int* sred) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (nwords + kBlockThreads - 1) / kBlockThreads;
@@ -113,7 +133,7 @@ __device__ inline int bitmap_prefix(const uint32_t* sbm, uint32_t* spre, int nwo
   for (int w = w0; w < w1; ++w) local += __popc(sbm[w]);
   int incl = wave_inclusive_scan(local, lane);
   if (lane == 63) sred[wave] = incl;
-  __syncthreads();
+  block_sync<kLdsOnly>();
   int wave_off = 0, total = 0;
 #pragma unroll
   for (int i = 0; i < kBlockThreads / kWave; ++i) {
@@ -125,7 +145,7 @@ __device__ inline int bitmap_prefix(const uint32_t* sbm, uint32_t* spre, int nwo
     spre[w] = (uint32_t)run;
     run += __popc(sbm[w]);
   }
-  __syncthreads();
+  block_sync<kLdsOnly>();
   return total;
 }
 

@@ -21,12 +21,27 @@ uint32_t fp16_threshold_pattern(float threshold);
 hipError_t launch_cols_from_bitmap(const uint32_t* bitmap, int64_t K, int32_t* cols,
                                    int32_t* n_out, hipStream_t s);
 
+// The layer's detection without a cleared bitmap: part[b][w] (bands x
+// ceil(K/32) words, every word written) holds the flags of row band b, rows
+// [b * ceil(M/bands), ...); the bitmap is their OR. flag_bands(M, K) is the
+// band count the layer uses (1 .. kMaxFlagBands, no band empty).
+constexpr int kMaxFlagBands = 16;
+int flag_bands(int64_t M, int64_t K);
+hipError_t launch_outlier_flag_bands(const uint16_t* X, int64_t M, int64_t K, uint32_t tau16,
+                                     int bands, uint32_t* part, hipStream_t s);
+
 // Row pass over X (or W): optional absmax quantization (Xq, sx), optional
 // gather of outlier columns (Xo), optional cols/n output from the first row's
 // block. bitmap == nullptr means no outlier columns.
 hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* bitmap,
                        int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                        hipStream_t s);
+// The same with the flags given as `bands` partial bitmaps (bands x
+// ceil(K/32) words, see launch_outlier_flag_bands); the first block also
+// writes their OR to bitmap_out when it is given.
+hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
+                              int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
+                              uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s);
 
 // Wo: the fp16 outlier weight columns [N, LD(n)] written by
 // launch_recover_outlier_w (or launch_gather_w_cols), or nullptr; with more

@@ -33,6 +33,29 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t val
   if (i < count) p[i] = value;
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Per-column maximum of the fp16 magnitude patterns of a 16-byte chunk (8
+// columns), folded into mx[4] (element 2i in the low half of mx[i], 2i+1 in
+// the high half).
+__device__ __forceinline__ void fold_abs8(u16x2 mx[4], const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    mx[i] = __builtin_elementwise_max(mx[i], __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+}
+
+// Bit e set when column e of the chunk has a maximum pattern >= tau16.
+__device__ __forceinline__ uint32_t flag_mask8(const u16x2 mx[4], uint32_t tau16) {
+  uint32_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mask |= ((uint32_t)mx[i][0] >= tau16 ? 1u : 0u) << (2 * i);
+    mask |= ((uint32_t)mx[i][1] >= tau16 ? 1u : 0u) << (2 * i + 1);
+  }
+  return mask;
+}
+
 // Column OR-reduce. Block = 4 waves over one 512-column group; lane owns an
 // 8-column chunk; wave w scans rows r0+w, r0+w+4, ... of the block's row
 // range, keeping the per-column maximum of the fp16 magnitude bit patterns
@@ -58,31 +81,17 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = col_ok ? min(M, r0 + (int64_t)rows_per_block) : r0;
   const uint16_t* base = X + (col_ok ? col0 : 0);
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   u16x2 mx[4] = {u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}};
-  auto fold = [&](const uint4& v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u16x2 a = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
-      mx[i] = __builtin_elementwise_max(mx[i], a);
-    }
-  };
   int64_t r = r0 + wave;
   for (; r + 12 < r1; r += 16) {
     const uint4 v0 = ld16(base + r * K);
     const uint4 v1 = ld16(base + (r + 4) * K);
     const uint4 v2 = ld16(base + (r + 8) * K);
     const uint4 v3 = ld16(base + (r + 12) * K);
-    fold(v0); fold(v1); fold(v2); fold(v3);
+    fold_abs8(mx, v0); fold_abs8(mx, v1); fold_abs8(mx, v2); fold_abs8(mx, v3);
   }
-  for (; r < r1; r += 4) fold(ld16(base + r * K));
-  uint32_t mask = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mask |= ((uint32_t)mx[i][0] >= tau16 ? 1u : 0u) << (2 * i);
-    mask |= ((uint32_t)mx[i][1] >= tau16 ? 1u : 0u) << (2 * i + 1);
-  }
+  for (; r < r1; r += 4) fold_abs8(mx, ld16(base + r * K));
+  uint32_t mask = flag_mask8(mx, tau16);
   if (!col_ok) mask = 0;   // (with threshold 0 an empty max would pass)
   uint32_t word = mask << (col0 & 31);
   word |= (uint32_t)__shfl_xor((int)word, 1, kWave);
@@ -97,6 +106,54 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
       const uint32_t cur = __atomic_load_n(&bitmap[widx], __ATOMIC_RELAXED);
       if ((cur & w) != w) atomicOr(&bitmap[widx], w);
     }
+  }
+}
+
+// The layer's detection, without atomics: the rows are split into `bands`
+// row bands, and block (g, b) writes the 4 flag words of 128-column group g
+// over band b's rows to part[b][4g .. 4g+3] with plain stores, zero words
+// included, so the partial words need no clearing beforehand; the row pass
+// ORs the bands of each word. Lane (row slot, 16-lane column slot): 16 lanes
+// cover a group's 256 bytes of one row, a wavefront 4 rows and the block 16
+// rows per pass, 8 passes in flight per lane. The flag test is the one above.
+constexpr int kFlagGroupCols = 128;
+__global__ __launch_bounds__(256) void k_outlier_flag_bands(const uint16_t* __restrict__ X,
+                                                            int64_t M, int64_t K, uint32_t tau16,
+                                                            int64_t rows_per_band, int64_t nwords,
+                                                            uint32_t* __restrict__ part) {
+  __shared__ uint32_t s_word[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15;
+  const int64_t col0 = (int64_t)blockIdx.x * kFlagGroupCols + sub * 8;
+  const bool col_ok = col0 < K;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_band;
+  const int64_t r1 = col_ok ? min(M, r0 + rows_per_band) : r0;
+  const uint16_t* base = X + (col_ok ? col0 : 0);
+  u16x2 mx[4] = {u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}, u16x2{0, 0}};
+  int64_t r = r0 + wave * 4 + (lane >> 4);
+  for (; r + 112 < r1; r += 128) {
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ld16(base + (r + 16 * i) * K);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fold_abs8(mx, v[i]);
+  }
+  for (; r < r1; r += 16) fold_abs8(mx, ld16(base + r * K));
+  uint32_t mask = flag_mask8(mx, tau16);
+  if (!col_ok || r0 >= M) mask = 0;   // (with threshold 0 an empty max would pass)
+  // the four rows of a wavefront at one column slot, then the 4 slots of a word
+  mask |= (uint32_t)__shfl_xor((int)mask, 16, kWave);
+  mask |= (uint32_t)__shfl_xor((int)mask, 32, kWave);
+  uint32_t word = mask << ((sub & 3) * 8);
+  word |= (uint32_t)__shfl_xor((int)word, 1, kWave);
+  word |= (uint32_t)__shfl_xor((int)word, 2, kWave);
+  if (lane < 16 && (lane & 3) == 0) s_word[wave][lane >> 2] = word;
+  __syncthreads();
+  if (tid < 4) {
+    const int64_t widx = (int64_t)blockIdx.x * 4 + tid;
+    if (widx < nwords)
+      part[(int64_t)blockIdx.y * nwords + widx] =
+          s_word[0][tid] | s_word[1][tid] | s_word[2][tid] | s_word[3][tid];
   }
 }
 
@@ -133,13 +190,19 @@ __global__ __launch_bounds__(256) void k_cols_from_bitmap(const uint32_t* __rest
 // The absmax is taken on the fp16 bit patterns with the sign cleared: for
 // non-NaN values the unsigned order of those patterns is the order of the
 // magnitudes, and the maximum is exact.
-template <int CPT>
+// Flag source of the row pass: none (weight rows), one bitmap, or the
+// layer's per-band partial words.
+enum RowFlags { kNoFlags = 0, kBitmap = 1, kBands = 2 };
+
+template <int CPT, int FMODE>
 __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, int64_t M,
                                               int64_t K, int rows_per_block,
-                                              const uint32_t* __restrict__ bitmap,
+                                              const uint32_t* __restrict__ flags, int bands,
+                                              uint32_t* __restrict__ bitmap_out,
                                               int8_t* __restrict__ Xq, float* __restrict__ sx,
                                               uint16_t* __restrict__ Xo, int32_t* __restrict__ cols,
                                               int32_t* __restrict__ n_out) {
+  constexpr bool kFlags = FMODE != kNoFlags;
   extern __shared__ uint32_t smem[];
   __shared__ int sred[kRowThreads / kWave];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -148,59 +211,123 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   const int64_t nchunks = K / 8;
   uint32_t* sbm = smem;
   uint32_t* spre = smem + nwords;
-
   const int64_t row_lo = (int64_t)blockIdx.x * rows_per_block;
   const int64_t row_hi = min(M, row_lo + rows_per_block);
-  // The first row's loads are issued before the bitmap is staged, so the two
-  // global round trips overlap; later rows are prefetched one row ahead.
+  const int64_t row0 = row_lo + wave;
+
+  if (nchunks == 0) {   // K == 0: empty rows (absmax 0), no outlier columns
+    if (Xq && lane == 0)
+      for (int64_t row = row0; row < row_hi; row += kRowThreads / kWave) sx[row] = 0.0f;
+    if (blockIdx.x == 0 && tid == 0 && n_out) *n_out = 0;
+    return;
+  }
+
+  // The flag words are loaded first, then the first row, and the flags are
+  // only combined after that, so waiting for them leaves the row's loads in
+  // flight. Every load is unconditional, indices clamped into range (a
+  // clamped chunk is masked out below; a wave without a row in the last block
+  // reads that block's last row again): loads under a branch would leave the
+  // compiler unsure how many are outstanding, and it would wait for all.
+  constexpr int NFL = FMODE == kBands ? kMaxFlagBands : 1;
+  const int wi = tid < nwords ? tid : nwords - 1;
+  uint32_t fl[NFL];
+  if constexpr (kFlags) {
+#pragma unroll
+    for (int b = 0; b < NFL; ++b) fl[b] = flags[(int64_t)(b < bands ? b : 0) * nwords + wi];
+  }
+  asm volatile("" ::: "memory");   // the flag loads go out before the row's
   uint4 v[CPT > 0 ? CPT : 1];
   auto load_row = [&](int64_t row) {
     if constexpr (CPT > 0) {
       const uint16_t* xr = X + row * K;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        const int64_t c = lane + (int64_t)j * kWave;
-        v[j] = (row < row_hi && c < nchunks) ? ld16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        const int64_t c = min(lane + (int64_t)j * kWave, nchunks - 1);
+        v[j] = ld16(xr + c * 8);
       }
     }
   };
-  load_row(row_lo + wave);
+  load_row(row0 < row_hi ? row0 : row_hi - 1);
 
   int n = 0;
-  if (bitmap) {
-    for (int w = tid; w < nwords; w += kRowThreads) sbm[w] = bitmap[w];
-    __syncthreads();
-    if (Xo || cols || n_out) n = bitmap_prefix(sbm, spre, nwords, sred);
+  if constexpr (kFlags) {
+    uint32_t fw = 0;
+#pragma unroll
+    for (int b = 0; b < NFL; ++b) fw |= fl[b];
+    // unconditional (threads past the last word store that word's own value
+    // again), so the loads above cannot be moved into a branch
+    sbm[wi] = fw;
+    for (int w = tid + kRowThreads; w < nwords; w += kRowThreads) {
+      uint32_t o = 0;
+      for (int b = 0; b < bands; ++b) o |= flags[(int64_t)b * nwords + w];
+      sbm[w] = o;
+    }
+    // LDS-only barriers: the first row's loads stay in flight meanwhile
+    lds_only_barrier();
+    if (Xo || cols || n_out) n = bitmap_prefix<true>(sbm, spre, nwords, sred);
   }
   if (blockIdx.x == 0) {
-    if (bitmap) write_cols(sbm, spre, nwords, n, cols, n_out);
-    else if (n_out && tid == 0) *n_out = 0;
+    if constexpr (kFlags) {
+      write_cols(sbm, spre, nwords, n, cols, n_out);
+      if (bitmap_out)
+        for (int w = tid; w < nwords; w += kRowThreads) bitmap_out[w] = sbm[w];
+    } else {
+      if (n_out && tid == 0) *n_out = 0;
+    }
   }
   auto outl8 = [&](int64_t c) -> uint32_t {
-    if (!bitmap) return 0u;
+    if constexpr (!kFlags) return 0u;
     const int64_t k = c * 8;
     return (sbm[k >> 5] >> (k & 31)) & 0xffu;
   };
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
 
+  // Position in Xo of chunk c's first outlier column (its rank among them).
+  auto rank8 = [&](int64_t c) -> int {
+    const int64_t k0 = c * 8;
+    return (int)spre[k0 >> 5] + __popc(sbm[k0 >> 5] & ((1u << (k0 & 31)) - 1u));
+  };
+  // With the row in registers (CPT > 0) the chunks a lane holds are the same
+  // for every row, so their outlier masks and Xo positions are taken from
+  // LDS once, while the first row is still in flight: meta[j] = rank << 8 |
+  // mask (0 for a clamped chunk).
+  uint32_t meta[CPT > 0 ? CPT : 1];
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t c = lane + (int64_t)j * kWave;
+      const uint32_t om = c < nchunks ? outl8(c) : 0u;
+      meta[j] = om ? ((Xo ? (uint32_t)rank8(c) << 8 : 0u) | om) : 0u;
+    }
+  }
+
+  // Element e of a chunk (e = 0..7): v_perm_b32 picks bytes 2(e%4), 2(e%4)+1
+  // of words (x, y) and of (z, w) (selector byte 0x0c gives 0), then e/4
+  // chooses. Selecting among the words themselves would make the compiler
+  // address the row array in memory (scratch) instead of registers.
+  auto pick_half = [](const uint4& t, int e) -> uint32_t {
+    const uint32_t h = (uint32_t)(e & 3) * 2u;
+    const uint32_t sel = 0x0c0c0000u | ((h + 1u) << 8) | h;
+    const uint32_t p01 = __builtin_amdgcn_perm(t.y, t.x, sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(t.w, t.z, sel);
+    return (e & 4) ? p23 : p01;
+  };
   // Outlier elements of a chunk: gather them to Xo (rare path), then zero
   // them in the register copy, so the absmax and the codes below need no
   // per-element test (a zero element has magnitude 0 and code 0).
-  auto strip = [&](int64_t row, int64_t c, uint4& t) {
-    const uint32_t om = outl8(c);
+  // m = rank << 8 | mask, as in meta.
+  auto strip = [&](int64_t row, uint32_t m, uint4& t) {
+    const uint32_t om = m & 0xffu;
     if (om) {
-      const int64_t k0 = c * 8;
-      const int pos0 = Xo ? (int)spre[k0 >> 5] + __popc(sbm[k0 >> 5] & ((1u << (k0 & 31)) - 1u)) : 0;
-      if (Xo && om == 0xffu && (pos0 & 7) == 0) {
-        // 8 outlier columns in a row land at 8 consecutive aligned positions
-        st16(Xo + row * ld + pos0, t);
-      } else if (Xo) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if ((om >> e) & 1u) {
-            const int pos = pos0 + __popc(om & ((1u << e) - 1u));
-            Xo[row * ld + pos] = (uint16_t)half_of(t, e);
-          }
+      if (Xo) {
+        int pos = (int)(m >> 8);
+        uint16_t* dst = Xo + row * ld;
+        if (om == 0xffu && (pos & 7) == 0) {
+          // 8 outlier columns in a row land at 8 consecutive aligned positions
+          st16(dst + pos, t);
+        } else {
+          for (uint32_t bits = om; bits; bits &= bits - 1u)
+            dst[pos++] = (uint16_t)pick_half(t, __builtin_ctz(bits));
         }
       }
       uint32_t w[4] = {t.x, t.y, t.z, t.w};
@@ -213,7 +340,6 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
       t = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   auto absmax_fold = [&](u16x2 m, const uint4& t) -> u16x2 {
     const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
@@ -223,20 +349,21 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   };
   auto codes8 = [](const uint4& t, float s) -> uint2 { return codes8_rne(t, s); };
 
-  for (int64_t row = row_lo + wave; row < row_hi; row += kRowThreads / kWave) {
+  for (int64_t row = row0; row < row_hi; row += kRowThreads / kWave) {
     const uint16_t* xr = X + row * K;
     u16x2 m2 = u16x2{0, 0};
     if constexpr (CPT > 0) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        const int64_t c = lane + (int64_t)j * kWave;
-        if (c < nchunks) strip(row, c, v[j]);
-        m2 = absmax_fold(m2, v[j]);
+        const bool ok = lane + (int64_t)j * kWave < nchunks;
+        strip(row, meta[j], v[j]);
+        m2 = absmax_fold(m2, ok ? v[j] : make_uint4(0, 0, 0, 0));
       }
     } else {
       for (int64_t c = lane; c < nchunks; c += kWave) {
         uint4 t = ld16(xr + c * 8);
-        strip(row, c, t);
+        const uint32_t om = outl8(c);
+        if (om) strip(row, (Xo ? (uint32_t)rank8(c) << 8 : 0u) | om, t);
         m2 = absmax_fold(m2, t);
       }
     }
@@ -270,7 +397,56 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
     }
     if (Xo)
       for (int64_t t = n + lane; t < ld; t += kWave) Xo[row * ld + t] = 0;
-    load_row(row + kRowThreads / kWave);
+    if (row + kRowThreads / kWave < row_hi) load_row(row + kRowThreads / kWave);
+  }
+}
+
+template <int CPT>
+hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
+                         int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx, uint16_t* Xo,
+                         int32_t* cols, int32_t* n_out, hipStream_t s) {
+  const int nwords = (int)((K + 31) / 32);
+  const size_t shm = flags ? (size_t)nwords * 2 * sizeof(uint32_t) : 0;
+  // 4 rows per block (one per wavefront) while that keeps >= 1024 blocks;
+  // more rows per block beyond that amortize the bitmap prefix.
+  int64_t rpb = 4;
+  while (rpb < 64 && (M + rpb * 2 - 1) / (rpb * 2) >= 1024) rpb *= 2;
+  const int64_t blocks = (M + rpb - 1) / rpb;
+  auto kern = !flags ? k_rows<CPT, kNoFlags> : bands == 1 ? k_rows<CPT, kBitmap>
+                                                           : k_rows<CPT, kBands>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K, (int)rpb,
+                     flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out);
+  return hipGetLastError();
+}
+
+// Wo [N, LD(n)] is built one 16-byte piece (8 columns of a row) per thread,
+// the threads laid flat over the N * LD(n) / 8 (row, piece) items so that
+// consecutive threads fill consecutive pieces: with a few dozen outlier
+// columns a row is only a handful of pieces, and a block per row would
+// leave almost all of its threads idle and walk its rows one after another.
+// f(j, t0): row j, columns t0 .. t0+7.
+constexpr int kWoThreads = 256;
+template <class F>
+__device__ __forceinline__ void for_each_wo_piece(int64_t N, int64_t ld, F&& f) {
+  const int64_t per_row = ld / 8;
+  const int64_t items = N * per_row;
+  const int64_t stride = (int64_t)gridDim.x * kWoThreads;
+  for (int64_t it = (int64_t)blockIdx.x * kWoThreads + threadIdx.x; it < items; it += stride) {
+    const int64_t j = it / per_row;
+    f(j, (it - j * per_row) * 8);
+  }
+}
+
+// cols[t0 .. t0+7], -1 from n on (the zero pad).
+__device__ __forceinline__ void load_cols8(const int32_t* __restrict__ cols, int64_t t0, int n,
+                                           int c[8]) {
+  if (t0 + 8 <= n) {
+    const uint4 c0 = ld16(cols + t0), c1 = ld16(cols + t0 + 4);
+    c[0] = (int)c0.x; c[1] = (int)c0.y; c[2] = (int)c0.z; c[3] = (int)c0.w;
+    c[4] = (int)c1.x; c[5] = (int)c1.y; c[6] = (int)c1.z; c[7] = (int)c1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = t0 + e < n ? cols[t0 + e] : -1;
   }
 }
 
@@ -280,81 +456,50 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
 //   Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127))  for t < n,
 //   +0.0 for n <= t < LD(n), rows LD(n) halfs apart.
 // n is read on the device; with 16 or fewer outlier columns the GEMM stages
-// them itself and this does nothing. One block per (row, 2048-column chunk)
-// task. The value depends only on the code q and the row, and is odd in q
-// (each of the three roundings is symmetric), so the block computes the
-// values of q = 0..128 with the exact arithmetic into LDS, then each thread
-// builds 8 consecutive columns by lookup (sign bit from the code) and stores
-// them as one 16-byte write.
-constexpr int kRecoverCols = 2048;   // columns per block: 256 threads x 8
-__global__ __launch_bounds__(256) void k_recover_outlier_w(
+// them itself and this does nothing.
+__global__ __launch_bounds__(kWoThreads) void k_recover_outlier_w(
     const int8_t* __restrict__ Wq, const float* __restrict__ sw, int64_t N, int64_t K,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     uint16_t* __restrict__ Wo) {
-  __shared__ uint16_t s_lut[130];   // q = 0..128 (-128 is a valid int8)
   const int n = *n_out;
   if (n <= 16) return;
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-  const int64_t chunks = (ld + kRecoverCols - 1) / kRecoverCols;
-  const int tid = threadIdx.x;
-  for (int64_t task = blockIdx.x; task < N * chunks; task += gridDim.x) {
-    const int64_t j = task / chunks;
-    const int64_t t0 = (task - j * chunks) * kRecoverCols + (int64_t)tid * 8;
-    // this thread's column indices and codes are fetched before the table
-    // is built, so their latency overlaps it
+  for_each_wo_piece(N, ld, [&](int64_t j, int64_t t0) {
     int c[8];
-    if (t0 + 8 <= n) {
-      const uint4 c0 = ld16(cols + t0), c1 = ld16(cols + t0 + 4);
-      c[0] = (int)c0.x; c[1] = (int)c0.y; c[2] = (int)c0.z; c[3] = (int)c0.w;
-      c[4] = (int)c1.x; c[5] = (int)c1.y; c[6] = (int)c1.z; c[7] = (int)c1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = t0 + e < n ? cols[t0 + e] : -1;
-    }
+    load_cols8(cols, t0, n, c);
     const int8_t* row = Wq + j * K;
     int q[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = c[e] >= 0 ? (int)row[c[e]] : 0;
-    __syncthreads();   // the previous task's lookups are done
-    if (tid <= 128) s_lut[tid] = f2h(((float)tid * sw[j]) / 127.0f);
-    __syncthreads();
-    if (t0 < ld) {
-      uint32_t h[8];
+    const float s = sw[j];
+    uint32_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t mag = s_lut[q[e] < 0 ? -q[e] : q[e]];
-        h[e] = c[e] >= 0 ? (mag | (q[e] < 0 ? 0x8000u : 0u)) : 0u;
-      }
-      st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                        h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
-    }
-  }
+    for (int e = 0; e < 8; ++e) h[e] = c[e] >= 0 ? f2h(((float)q[e] * s) / 127.0f) : 0u;
+    st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                      h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
+  });
 }
 
 // Outlier weight columns of a layer that keeps its weight in fp16 ([HF-blog]
 // "Usage", has_fp16_weights=True): Wo[j, t] = W[j, cols[t]] as they are, for
-// t < n, +0.0 up to LD(n), 8 columns per thread over the same (row, column
-// chunk) tasks as the recovery above. Nothing when n <= 16 (the GEMM stages
-// those itself).
-__global__ __launch_bounds__(256) void k_gather_w_cols(const uint16_t* __restrict__ W, int64_t N,
-                                                      int64_t K, const int32_t* __restrict__ cols,
-                                                      const int32_t* __restrict__ n_out,
-                                                      uint16_t* __restrict__ Wo) {
+// t < n, +0.0 up to LD(n), with the same pieces as the recovery above.
+// Nothing when n <= 16 (the GEMM stages those itself).
+__global__ __launch_bounds__(kWoThreads) void k_gather_w_cols(
+    const uint16_t* __restrict__ W, int64_t N, int64_t K, const int32_t* __restrict__ cols,
+    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Wo) {
   const int n = *n_out;
   if (n <= 16) return;
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-  const int64_t chunks = (ld + kRecoverCols - 1) / kRecoverCols;
-  for (int64_t task = blockIdx.x; task < N * chunks; task += gridDim.x) {
-    const int64_t j = task / chunks;
-    const int64_t t0 = (task - j * chunks) * kRecoverCols + (int64_t)threadIdx.x * 8;
-    if (t0 >= ld) continue;
+  for_each_wo_piece(N, ld, [&](int64_t j, int64_t t0) {
+    int c[8];
+    load_cols8(cols, t0, n, c);
     const uint16_t* row = W + j * K;
     uint32_t h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = t0 + e < n ? (uint32_t)row[cols[t0 + e]] : 0u;
+    for (int e = 0; e < 8; ++e) h[e] = c[e] >= 0 ? (uint32_t)row[c[e]] : 0u;
     st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
-  }
+  });
 }
 
 // Exact-erf GELU in fp32 (activation between the two layers of an MLP block).
@@ -368,21 +513,6 @@ __global__ void k_gelu(const uint16_t* __restrict__ X, int64_t count, uint16_t* 
   Y[i] = f2h(y);
 }
 
-template <int CPT>
-hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* bitmap,
-                         int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
-                         hipStream_t s) {
-  const int nwords = (int)((K + 31) / 32);
-  const size_t shm = bitmap ? (size_t)nwords * 2 * sizeof(uint32_t) : 0;
-  // 4 rows per block (one per wavefront) while that keeps >= 1024 blocks;
-  // more rows per block beyond that amortize the bitmap prefix.
-  int64_t rpb = 4;
-  while (rpb < 64 && (M + rpb * 2 - 1) / (rpb * 2) >= 1024) rpb *= 2;
-  const int64_t blocks = (M + rpb - 1) / rpb;
-  hipLaunchKernelGGL(k_rows<CPT>, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K,
-                     (int)rpb, bitmap, Xq, sx, Xo, cols, n_out);
-  return hipGetLastError();
-}
 
 }  // namespace
 
@@ -434,40 +564,74 @@ hipError_t launch_cols_from_bitmap(const uint32_t* bitmap, int64_t K, int32_t* c
   return hipGetLastError();
 }
 
+hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
+                              int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
+                              uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+#define I8MM_ROWS(CPT) \
+  launch_rows_t<CPT>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, s)
+  if (per_lane <= 1) return I8MM_ROWS(1);
+  if (per_lane <= 2) return I8MM_ROWS(2);
+  if (per_lane <= 4) return I8MM_ROWS(4);
+  if (per_lane <= 8) return I8MM_ROWS(8);
+  if (per_lane <= 16) return I8MM_ROWS(16);
+  if (per_lane <= 24) return I8MM_ROWS(24);
+  if (per_lane <= 32) return I8MM_ROWS(32);
+  return I8MM_ROWS(0);
+#undef I8MM_ROWS
+}
+
 hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* bitmap,
                        int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                        hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-  if (per_lane <= 1) return launch_rows_t<1>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 2) return launch_rows_t<2>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 4) return launch_rows_t<4>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 8) return launch_rows_t<8>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 16) return launch_rows_t<16>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 24) return launch_rows_t<24>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  if (per_lane <= 32) return launch_rows_t<32>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
-  return launch_rows_t<0>(X, M, K, bitmap, Xq, sx, Xo, cols, n_out, s);
+  return launch_rows_banded(X, M, K, bitmap, 1, nullptr, Xq, sx, Xo, cols, n_out, s);
+}
+
+int flag_bands(int64_t M, int64_t K) {
+  const int64_t nwords = (K + 31) / 32;
+  if (M <= 0 || nwords == 0) return 1;
+  // about 2048 partial words in all: few loads per word in the row pass
+  int64_t b = std::min<int64_t>(kMaxFlagBands, std::max<int64_t>(1, 2048 / nwords));
+  // at least one pass of 16 rows per band
+  b = std::min<int64_t>(b, std::max<int64_t>(1, M / 16));
+  // no empty band: ceil(M / ceil(M / b)) bands of ceil(M / b) rows
+  const int64_t rpb = (M + b - 1) / b;
+  return (int)((M + rpb - 1) / rpb);
+}
+
+hipError_t launch_outlier_flag_bands(const uint16_t* X, int64_t M, int64_t K, uint32_t tau16,
+                                     int bands, uint32_t* part, hipStream_t s) {
+  if (M <= 0 || K <= 0) return hipSuccess;
+  const int64_t rows_per_band = (M + bands - 1) / bands;
+  const int64_t groups = (K + kFlagGroupCols - 1) / kFlagGroupCols;
+  hipLaunchKernelGGL(k_outlier_flag_bands, dim3((unsigned)groups, (unsigned)bands), dim3(256), 0,
+                     s, X, M, K, tau16, rows_per_band, (K + 31) / 32, part);
+  return hipGetLastError();
+}
+
+// Blocks for the Wo builders: n is only known on the device, so the grid is
+// sized for the largest n (K columns), at most 2048 blocks (a grid-stride
+// loop covers the rest); blocks past the last piece exit at once.
+static unsigned wo_blocks(int64_t N, int64_t K) {
+  const int64_t pieces = N * (I8MM_OUTLIER_LD(K) / 8);
+  return (unsigned)std::min<int64_t>((pieces + kWoThreads - 1) / kWoThreads, 2048);
 }
 
 hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N, int64_t K,
                                     const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
                                     hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  // enough blocks for one (row, column chunk) task each at the largest n
-  const int64_t max_tasks = N * ((I8MM_OUTLIER_LD(K) + kRecoverCols - 1) / kRecoverCols);
-  const int64_t blocks = std::min<int64_t>(max_tasks, 2048);
-  hipLaunchKernelGGL(k_recover_outlier_w, dim3((unsigned)blocks), dim3(256), 0, s, Wq, sw, N, K,
-                     cols, n_out, Wo);
+  hipLaunchKernelGGL(k_recover_outlier_w, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wq, sw,
+                     N, K, cols, n_out, Wo);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
                                 const int32_t* n_out, uint16_t* Wo, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const int64_t max_tasks = N * ((I8MM_OUTLIER_LD(K) + kRecoverCols - 1) / kRecoverCols);
-  const int64_t blocks = std::min<int64_t>(max_tasks, 2048);
-  hipLaunchKernelGGL(k_gather_w_cols, dim3((unsigned)blocks), dim3(256), 0, s, Wf, N, K, cols,
-                     n_out, Wo);
+  hipLaunchKernelGGL(k_gather_w_cols, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wf, N, K,
+                     cols, n_out, Wo);
   return hipGetLastError();
 }
 

@@ -225,11 +225,15 @@ def gelu_f16(X, out=None):
     return Y
 
 
-def workspace_views(workspace, M, K):
-    """Typed views of the intermediates inside a linear_int8_mixed workspace."""
+def workspace_views(workspace, M, K, N=None):
+    """Typed views of the intermediates inside a linear_int8_mixed workspace.
+    Given N and a workspace of workspace_bytes(M, K, N), also "Wo": the fp16
+    outlier weight columns the tiled path materializes with more than 16
+    outlier columns, N rows outlier_ld(n) halfs apart (flat, capacity
+    N * outlier_ld(K))."""
     off = workspace_offsets(M, K)
     w = workspace
-    return {
+    views = {
         "bitmap": w[off["bitmap"]:off["bitmap"] + ((K + 31) // 32) * 4].view(torch.int32),
         "cols": w[off["cols"]:off["cols"] + K * 4].view(torch.int32),
         "n": w[off["n"]:off["n"] + 4].view(torch.int32),
@@ -237,3 +241,9 @@ def workspace_views(workspace, M, K):
         "Xq": w[off["Xq"]:off["Xq"] + M * K].view(torch.int8).view(M, K),
         "Xo": w[off["Xo"]:off["Xo"] + M * outlier_ld(K) * 2].view(torch.float16),
     }
+    if N is not None:
+        end = off["total"] + int(N) * outlier_ld(K) * 2
+        if workspace.numel() < end:
+            raise ValueError("workspace has no outlier weight region for N=%d" % N)
+        views["Wo"] = w[off["total"]:end].view(torch.float16)
+    return views

@@ -56,7 +56,7 @@ def _run(gpu, X, W, tau, b, big_ws, quantize=True, Wq0=None, sw0=None):
     Y = ops.linear_int8_mixed_fp16_weights(dev(X), dev(W), Wq, sw, quantize,
                                            None if b is None else dev(b), tau, ws)
     torch.cuda.synchronize()
-    return host(Y), host(Wq), host(sw), ops.workspace_views(ws, M, K)
+    return host(Y), host(Wq), host(sw), ops.workspace_views(ws, M, K, N if big_ws else None)
 
 
 def _check(gpu, X, W, ref, Y, Wq, sw, views):
@@ -99,6 +99,13 @@ def test_fp16_weights_layer(gpu, case):
     assert _discriminates(X, W, 6.0, b, ref)
     Y, Wq, sw, views = _run(gpu, X, W, 6.0, b, big)
     _check(gpu, X, W, ref, Y, Wq, sw, views)
+    if big and case.startswith("gemm") and ref["n"] > 16:
+        # the tiled path's materialized fp16 weight columns, bit for bit,
+        # and their zero pad
+        n, ld = ref["n"], gpu.ops.outlier_ld(ref["n"])
+        Wo = host(views["Wo"])[: N * ld].reshape(N, ld).view(np.uint16)
+        assert np.array_equal(Wo[:, :n], W[:, ref["cols"]].view(np.uint16))
+        assert not Wo[:, n:].any()
 
 
 @pytest.mark.parametrize("M", [40, 300])

@@ -284,17 +284,20 @@ def test_linear_edge_cases(gpu, case):
 
 
 @pytest.mark.parametrize("case", ["n17", "n33", "n100", "all_columns", "large_tiles_n40",
-                                  "large_tiles_all"])
+                                  "large_tiles_all", "wide_all"])
 def test_linear_many_outliers_fast_path(gpu, case):
     """More than 16 outlier columns with the larger workspace: the recovered
     outlier weights are materialized and the outlier product runs as a second
     GEMM main loop (all columns outliers: the int8 loop is skipped). Checked
     against the oracle, and bit for bit against the small-workspace path,
-    which adds the same fp16 MFMA products in the same order in the epilogue."""
+    which adds the same fp16 MFMA products in the same order in the epilogue.
+    wide_all: N * LD(K) / 8 = 1.07M 16-byte pieces of recovered weights,
+    more than the recovery's grid covers in one pass."""
     note("linear many outliers %s" % case)
     rng = np.random.default_rng(300 + len(case))
     large = case.startswith("large_tiles")
-    M, K, N = (4100, 528, 4100) if large else (200, 1040, 300)
+    M, K, N = (4100, 528, 4100) if large else (300, 2064, 4100) if case == "wide_all" \
+        else (200, 1040, 300)
     X = synth.normal_f16(rng, (M, K), 1.0)
     W = synth.normal_f16(rng, (N, K), 0.05)
     tau = 6.0
@@ -314,7 +317,14 @@ def test_linear_many_outliers_fast_path(gpu, case):
     Y_fast = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_big)
     Y_slow = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_small)
     torch.cuda.synchronize()
-    _check_intermediates(gpu, ops.workspace_views(ws_big, M, K), X, ref)
+    views = ops.workspace_views(ws_big, M, K, N)
+    _check_intermediates(gpu, views, X, ref)
+    # the recovered weights, bit for bit, and their zero pad
+    n, ld = ref["n"], ops.outlier_ld(ref["n"])
+    Wo = host(views["Wo"])[: N * ld].reshape(N, ld).view(np.uint16)
+    Wo_ref = O.recover_outlier_weights(Wq, sw, ref["cols"]).view(np.uint16)
+    assert np.array_equal(Wo[:, :n], Wo_ref)
+    assert not Wo[:, n:].any()
     assert y_err(host(Y_fast), ref["Y"]) <= Y_TOL
     assert np.array_equal(host(Y_fast).view(np.uint16), host(Y_slow).view(np.uint16))
 
