@@ -456,28 +456,66 @@ __device__ __forceinline__ void load_cols8(const int32_t* __restrict__ cols, int
 //   Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127))  for t < n,
 //   +0.0 for n <= t < LD(n), rows LD(n) halfs apart.
 // n is read on the device; with 16 or fewer outlier columns the GEMM stages
-// them itself and this does nothing.
+// them itself and this does nothing. Up to 96 columns (LD(n) <= 96) each
+// thread computes its 8 values directly over the flat pieces. Beyond that a
+// row has enough columns for a table to pay: the value depends only on the
+// code q and the row and is odd in q (each of the three roundings is
+// symmetric), so a block takes one row (up to 2048 columns) at a time, builds
+// the values of q = 0..128 with the same arithmetic in LDS, and each thread
+// looks up its 8 (sign bit from the code). Both give the same bits.
+constexpr int kRecoverCols = 2048;   // columns per block and row: 256 threads x 8
 __global__ __launch_bounds__(kWoThreads) void k_recover_outlier_w(
     const int8_t* __restrict__ Wq, const float* __restrict__ sw, int64_t N, int64_t K,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     uint16_t* __restrict__ Wo) {
+  __shared__ uint16_t s_lut[130];   // q = 0..128 (-128 is a valid int8)
   const int n = *n_out;
   if (n <= 16) return;
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-  for_each_wo_piece(N, ld, [&](int64_t j, int64_t t0) {
-    int c[8];
+  auto codes = [&](int64_t j, int64_t t0, int c[8], int q[8]) {
     load_cols8(cols, t0, n, c);
     const int8_t* row = Wq + j * K;
-    int q[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = c[e] >= 0 ? (int)row[c[e]] : 0;
-    const float s = sw[j];
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = c[e] >= 0 ? f2h(((float)q[e] * s) / 127.0f) : 0u;
+  };
+  auto store = [&](int64_t j, int64_t t0, const uint32_t h[8]) {
     st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
-  });
+  };
+  if (ld <= 96) {
+    for_each_wo_piece(N, ld, [&](int64_t j, int64_t t0) {
+      int c[8], q[8];
+      codes(j, t0, c, q);
+      const float s = sw[j];
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = c[e] >= 0 ? f2h(((float)q[e] * s) / 127.0f) : 0u;
+      store(j, t0, h);
+    });
+    return;
+  }
+  const int64_t chunks = (ld + kRecoverCols - 1) / kRecoverCols;
+  const int tid = threadIdx.x;
+  for (int64_t task = blockIdx.x; task < N * chunks; task += gridDim.x) {
+    const int64_t j = task / chunks;
+    const int64_t t0 = (task - j * chunks) * kRecoverCols + (int64_t)tid * 8;
+    // the codes are fetched before the table is built, so their latency
+    // overlaps it
+    int c[8], q[8];
+    if (t0 < ld) codes(j, t0, c, q);
+    __syncthreads();   // the previous task's lookups are done
+    if (tid <= 128) s_lut[tid] = f2h(((float)tid * sw[j]) / 127.0f);
+    __syncthreads();
+    if (t0 < ld) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mag = s_lut[q[e] < 0 ? -q[e] : q[e]];
+        h[e] = c[e] >= 0 ? (mag | (q[e] < 0 ? 0x8000u : 0u)) : 0u;
+      }
+      store(j, t0, h);
+    }
+  }
 }
 
 // Outlier weight columns of a layer that keeps its weight in fp16 ([HF-blog]

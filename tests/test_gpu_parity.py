@@ -283,7 +283,7 @@ def test_linear_edge_cases(gpu, case):
         assert ref["n"] >= int(case[1:])
 
 
-@pytest.mark.parametrize("case", ["n17", "n33", "n100", "all_columns", "large_tiles_n40",
+@pytest.mark.parametrize("case", ["n17", "n33", "n70", "n100", "all_columns", "large_tiles_n40",
                                   "large_tiles_all", "wide_all"])
 def test_linear_many_outliers_fast_path(gpu, case):
     """More than 16 outlier columns with the larger workspace: the recovered
