@@ -39,6 +39,10 @@
  *   - K <= I8MM_MAX_K, the largest K for which sum_k q_x q_w cannot overflow
  *     int32 (127 * 127 * K < 2^31).
  *   - M == 0 or N == 0 is valid and does nothing (except where stated).
+ *   - K == 0 is valid: the products are empty sums (a layer returns Y = bias,
+ *     or 0), every row's absmax is 0 and no column is an outlier column.
+ *   - A pointer to an array with no elements (one of its sizes is 0) may be
+ *     NULL.
  *   - Calls are thread-safe; calls on one stream are ordered; calls that write
  *     the same buffers from different streams race.
  */

@@ -147,9 +147,9 @@ int int8_quantize_colwise_weight(const uint16_t* W, int64_t N, int64_t K, int8_t
                                  i8mm_stream_t stream) {
   const char* fn = "int8_quantize_colwise_weight";
   I8MM_TRY(check_dims(fn, N, 0, K));
-  I8MM_TRY(check_ptr(fn, "W", W, true));
-  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
-  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  I8MM_TRY(check_ptr(fn, "W", W, N * K > 0));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, N * K > 0));
+  I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
   if (N == 0) return ok();
   I8MM_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
@@ -161,10 +161,10 @@ int int8_quantize_rowwise(const uint16_t* X, int64_t M, int64_t K, const uint32_
                           int8_t* Xq, float* sx, i8mm_stream_t stream) {
   const char* fn = "int8_quantize_rowwise";
   I8MM_TRY(check_dims(fn, M, 0, K));
-  I8MM_TRY(check_ptr(fn, "X", X, true));
+  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
   I8MM_TRY(check_ptr(fn, "outlier_bitmap", outlier_bitmap, false));
-  I8MM_TRY(check_ptr(fn, "Xq", Xq, true));
-  I8MM_TRY(check_ptr(fn, "sx", sx, true));
+  I8MM_TRY(check_ptr(fn, "Xq", Xq, M * K > 0));
+  I8MM_TRY(check_ptr(fn, "sx", sx, M > 0));
   if (M == 0) return ok();
   I8MM_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
@@ -179,9 +179,9 @@ int outlier_detect_gather(const uint16_t* X, int64_t M, int64_t K, float thresho
   const char* fn = "outlier_detect_gather";
   I8MM_TRY(check_dims(fn, M, 0, K));
   if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
-  I8MM_TRY(check_ptr(fn, "X", X, M > 0));
-  I8MM_TRY(check_ptr(fn, "bitmap", bitmap, true));
-  I8MM_TRY(check_ptr(fn, "cols", cols, true));
+  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
+  I8MM_TRY(check_ptr(fn, "bitmap", bitmap, K > 0));
+  I8MM_TRY(check_ptr(fn, "cols", cols, K > 0));
   I8MM_TRY(check_ptr(fn, "n_outliers", n_outliers, true));
   I8MM_TRY(check_ptr(fn, "Xo", Xo, false));
   I8MM_TRY(check_device());
@@ -202,10 +202,10 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
                     i8mm_stream_t stream) {
   const char* fn = "int8_mm_dequant";
   I8MM_TRY(check_dims(fn, M, N, K));
-  I8MM_TRY(check_ptr(fn, "Xq", Xq, true));
-  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
-  I8MM_TRY(check_ptr(fn, "sx", sx, true));
-  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  I8MM_TRY(check_ptr(fn, "Xq", Xq, M * K > 0));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, N * K > 0));
+  I8MM_TRY(check_ptr(fn, "sx", sx, M > 0));
+  I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
   const bool any_o = Xo || cols || n_outliers;
   const bool all_o = Xo && cols && n_outliers;
   if (any_o && !all_o)
@@ -241,11 +241,11 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
               bool quantize_w) {
   I8MM_TRY(check_dims(fn, M, N, K));
   if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
-  I8MM_TRY(check_ptr(fn, "X", X, true));
-  I8MM_TRY(check_ptr(fn, "Wq", Wq, true));
-  I8MM_TRY(check_ptr(fn, "sw", sw, true));
+  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, N * K > 0));
+  I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
   I8MM_TRY(check_ptr(fn, "bias", bias, false));
-  I8MM_TRY(check_ptr(fn, "Y", Y, true));
+  I8MM_TRY(check_ptr(fn, "Y", Y, M * N > 0));
   int64_t off[7], off_part = 0;
   layout(M, K, off, &off_part);
   if (!workspace) return fail(I8MM_EWORKSPACE, "%s: workspace is NULL", fn);
@@ -314,7 +314,7 @@ int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_t K, cons
                                    void* workspace, size_t workspace_bytes,
                                    i8mm_stream_t stream) {
   const char* fn = "linear_int8_mixed_fp16_weights";
-  I8MM_TRY(check_ptr(fn, "W", W, true));
+  I8MM_TRY(check_ptr(fn, "W", W, N * K > 0));
   return run_layer(fn, X, M, K, Wq, sw, N, bias, threshold, Y, workspace, workspace_bytes,
                    (hipStream_t)stream, W, quantize_weight != 0);
 }
@@ -322,8 +322,8 @@ int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_t K, cons
 int i8mm_gelu_f16(const uint16_t* X, int64_t count, uint16_t* Y, i8mm_stream_t stream) {
   const char* fn = "i8mm_gelu_f16";
   if (count < 0) return fail(I8MM_EINVAL, "%s: negative count", fn);
-  I8MM_TRY(check_ptr(fn, "X", X, true));
-  I8MM_TRY(check_ptr(fn, "Y", Y, true));
+  I8MM_TRY(check_ptr(fn, "X", X, count > 0));
+  I8MM_TRY(check_ptr(fn, "Y", Y, count > 0));
   if (count == 0) return ok();
   I8MM_TRY(check_device());
   I8MM_TRY(launched(i8mm::launch_gelu(X, count, Y, (hipStream_t)stream), fn));

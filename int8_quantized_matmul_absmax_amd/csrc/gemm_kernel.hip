@@ -732,7 +732,9 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                        const uint16_t* Wo, const uint16_t* Wf, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (gemv_applies(M))
+  // (K == 0 goes to the tiled kernel, whose empty main loop leaves only the
+  // epilogue: Y = bias, or 0)
+  if (gemv_applies(M) && K > 0)
     return launch_gemv(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wf, s);
   // 256 x 256 tiles when they give every CU at least one; otherwise the
   // 128 x 128 tiles (four times as many, two blocks per CU).

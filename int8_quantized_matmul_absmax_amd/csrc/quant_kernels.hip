@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   const int64_t row0 = row_lo + wave;
 
   if (nchunks == 0) {   // K == 0: empty rows (absmax 0), no outlier columns
-    if (Xq && lane == 0)
+    if (sx && lane == 0)
       for (int64_t row = row0; row < row_hi; row += kRowThreads / kWave) sx[row] = 0.0f;
     if (blockIdx.x == 0 && tid == 0 && n_out) *n_out = 0;
     return;
@@ -659,7 +659,7 @@ static unsigned wo_blocks(int64_t N, int64_t K) {
 hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N, int64_t K,
                                     const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
                                     hipStream_t s) {
-  if (N <= 0) return hipSuccess;
+  if (N <= 0 || K <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_recover_outlier_w, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wq, sw,
                      N, K, cols, n_out, Wo);
   return hipGetLastError();
@@ -667,7 +667,7 @@ hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N
 
 hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
                                 const int32_t* n_out, uint16_t* Wo, hipStream_t s) {
-  if (N <= 0) return hipSuccess;
+  if (N <= 0 || K <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_gather_w_cols, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wf, N, K,
                      cols, n_out, Wo);
   return hipGetLastError();

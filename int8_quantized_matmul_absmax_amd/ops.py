@@ -12,6 +12,7 @@ Matrix Multiplication for Transformers at Scale".
 """
 
 import ctypes
+import math
 
 import torch
 
@@ -50,7 +51,7 @@ def _flatten_tokens(X):
     """[..., K] -> [M, K] (tokens of all leading dims are the rows)."""
     if X.dim() < 2:
         raise ValueError("X must be at least 2-D")
-    return X.reshape(-1, X.shape[-1])
+    return X.reshape(math.prod(X.shape[:-1]), X.shape[-1])   # (-1 is ambiguous when K == 0)
 
 
 def int8_quantize_colwise_weight(W, Wq=None, sw=None):

@@ -204,3 +204,33 @@ def test_python_ops_refuse_cpu_tensors():
         i8.ops.int8_quantize_colwise_weight(W)
     with pytest.raises(TypeError):
         i8.ops.int8_quantize_colwise_weight(W.float())
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="the calls would launch on placeholder pointers")
+def test_empty_arrays_may_be_null(lib):
+    """With K == 0, X, Wq (and W, Xq, bitmap, cols) hold no elements and may be
+    NULL: validation passes and the call only stops at the device check here.
+    With K > 0 the same NULLs are rejected."""
+    M, K, N = 8, 0, 32
+    need = lib.linear_int8_mixed_workspace_bytes(M, K)
+    ws = ctypes.c_void_p(0x100000)
+    nodev = _lib.I8MM_ENODEVICE
+    assert lib.linear_int8_mixed(NUL, M, K, NUL, A, N, NUL, 6.0, A2, ws, need, NUL) == nodev
+    assert lib.linear_int8_mixed(NUL, M, 64, NUL, A, N, NUL, 6.0, A2, ws,
+                                 lib.linear_int8_mixed_workspace_bytes(M, 64), NUL) == _lib.I8MM_EINVAL
+    assert lib.linear_int8_mixed_fp16_weights(NUL, M, K, NUL, N, NUL, A, 1, NUL, 6.0, A2, ws, need,
+                                              NUL) == nodev
+    assert lib.int8_quantize_colwise_weight(NUL, N, K, NUL, A, NUL) == nodev
+    assert lib.int8_quantize_rowwise(NUL, M, K, NUL, NUL, A, NUL) == nodev
+    assert lib.outlier_detect_gather(NUL, M, K, 6.0, NUL, NUL, A, NUL, NUL) == nodev
+    assert lib.int8_mm_dequant(NUL, NUL, A, A2, M, N, K, NUL, NUL, NUL, NUL, A, NUL, NUL) == nodev
+    assert lib.int8_mm_dequant(NUL, NUL, A, A2, M, N, 16, NUL, NUL, NUL, NUL, A, NUL,
+                               NUL) == _lib.I8MM_EINVAL

@@ -478,3 +478,41 @@ def test_int8_linear_save_load(gpu, tmp_path):
     lin3.load_state_dict(torch.load(sd, weights_only=True))
     assert lin3.quantized
     assert np.array_equal(host(lin3(dev(X))).view(np.uint16), Y0.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [3, 40, 300])
+def test_empty_k(gpu, M):
+    """K == 0: every product is an empty sum ([Summary] "The full picture" with
+    no hidden features). On each token path (few-token, GEMV range, tiled) the
+    layer returns Y = bias exactly, with no outlier column and every row
+    scale 0, as the oracle does; so do the fp16-weight layer and the step
+    calls (weight scales 0, C = 0)."""
+    note("empty K, M=%d" % M)
+    ops = _ops(gpu)
+    N = 150
+    X = np.zeros((M, 0), np.float16)
+    W = np.zeros((N, 0), np.float16)
+    bias = synth.normal_f16(np.random.default_rng(41), (N,), 0.5)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0, bias)
+    assert ref["n"] == 0
+    ref_bits = ref["Y"].astype(np.float16).view(np.uint16)
+    Wqd, swd = ops.int8_quantize_colwise_weight(dev(W))
+    ws = torch.empty((ops.workspace_bytes(M, 0),), dtype=torch.uint8, device="cuda")
+    Y = ops.linear_int8_mixed(dev(X), Wqd, swd, dev(bias), 6.0, ws)
+    torch.cuda.synchronize()
+    assert tuple(Wqd.shape) == (N, 0)
+    assert np.array_equal(host(swd).view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(host(Y).view(np.uint16), ref_bits)
+    views = ops.workspace_views(ws, M, 0)
+    assert int(host(views["n"])[0]) == 0
+    assert not host(views["sx"]).view(np.uint32).any()
+    Yw = ops.linear_int8_mixed_fp16_weights(dev(X), dev(W), Wqd, swd, True, dev(bias), 6.0, ws)
+    Xq, sx = ops.int8_quantize_rowwise(dev(X))
+    _, _, n, _ = ops.outlier_detect_gather(dev(X), 6.0)
+    Ys, C = ops.int8_mm_dequant(Xq, Wqd, sx, swd, bias=dev(bias), want_int32=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Yw).view(np.uint16), ref_bits)
+    assert not host(sx).view(np.uint32).any() and int(host(n)[0]) == 0
+    assert np.array_equal(host(Ys).view(np.uint16), ref_bits)
+    assert not host(C).any()
