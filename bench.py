@@ -104,7 +104,13 @@ def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y):
     from oracle import llm_int8 as O
     Wq_ref, sw_ref = O.quantize_weight_rows(d["W"])
     ref = O.linear_int8_mixed(d["X"], Wq_ref, sw_ref, 6.0, rows=rows_y)
+    Yr = np.asarray(ref["Y"], np.float64)
+    dY = np.abs(np.asarray(Y_rows, np.float64) - Yr)
+    floor = 1e-2 * np.abs(Yr).max()
     parity = {"y_max_abs_rel_err_sampled_rows": O.max_abs_rel_error(Y_rows, ref["Y"]),
+              # per element, relative to max(|Y_ref|, 1e-2 max |Y_ref|)
+              "y_elem_rel_err_floor_1e-2_sampled_rows":
+                  float((dY / np.maximum(np.abs(Yr), floor)).max()) if Yr.size else 0.0,
               "weight_codes_bitexact": bool(np.array_equal(Wq_gpu, Wq_ref))}
     try:
         from threadpoolctl import threadpool_info
@@ -131,9 +137,18 @@ def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y):
         calls += 1
     dt = total / calls
     tops = 2.0 * rows.size * N * K / dt / 1e12
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return ({"value": round(tops, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
              "sample": "%d of %d token rows x all %d outputs (outlier detection over all rows), "
-                       "%d call(s), %.2f s each" % (rows.size, M, N, calls, dt)}, parity)
+                       "%d call(s), %.2f s each" % (rows.size, M, N, calls, dt),
+             "host": {"cpu_model": model, "logical_cpus": os.cpu_count(),
+                      "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}, parity)
 
 
 COPY_PROBE_BYTES = 512 << 20
@@ -555,6 +570,18 @@ def main():
     wall = time.perf_counter() - t0
     eff_tops = 2.0 * M * N * K / (ms_step * 1e-3) / 1e12
 
+    # ---- per-step spread, from a separate pass with an event between steps
+    nsp = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsp + 1)]
+    evs[0].record(stream)
+    for i in range(nsp):
+        step(i)
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    step_us = np.sort([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(nsp)])
+    spread = {q: round(float(np.percentile(step_us, v)), 2)
+              for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     # ---- the dominant kernel alone: int8 GEMM + fused epilogue, same launch
     # configuration as inside the layer (intermediates from the last step)
     views = [ops.workspace_views(p["ws"], M, K) for p in pool]
@@ -612,6 +639,10 @@ def main():
                      "traffic": traffic, "ms_per_launch": round(ms_gemm, 6),
                      "ops_per_launch": 2 * M * N * K},
         "int8_mfma_peak_frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+        "step_us_spread": spread,
+        # the dense-equivalent count above split by arithmetic: int8 ops on the
+        # K - n normal columns, fp16 flops on the n outlier columns
+        "ops_split": {"int8_ops": 2 * M * N * (K - n_out), "fp16_flops": 2 * M * N * n_out},
         "quantize": {"x_rowwise_gbps": round(rowq_gbps, 1),
                      "x_rowwise_hbm_frac": round(rowq_gbps / PEAK_HBM_GBPS, 4),
                      "x_rowwise_ms": round(ms_rowq, 6),
