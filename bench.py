@@ -371,11 +371,16 @@ def _sweep():
             state["i"] += 1
             return ops.linear_int8_mixed(X, Wqs[state["i"] % copies], sw, None, 6.0, ws, Y)
         us, same = _graph_time_us(call, reps=copies)
+        # warm: the same weight copy every call, so it stays in the MALL
+        us_w, same_w = _graph_time_us(
+            lambda: ops.linear_int8_mixed(X, Wq, sw, None, 6.0, ws, Y), reps=copies)
         bytes_w = N * K + 4 * N
         emit({"case": name, "M": M, "K": K, "N": N, "us_per_layer": round(us, 3),
               "weight_stream_gbps": round(bytes_w / (us * 1e-6) / 1e9, 1),
               "eff_tops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 4),
-              "timing": "hip graph of %d calls" % copies, "replays_identical": same})
+              "us_per_layer_warm_mall_resident": round(us_w, 3),
+              "timing": "hip graph of %d calls (weight rotated over %d copies; warm: one copy)"
+                        % (copies, copies), "replays_identical": bool(same and same_w)})
         del Wqs, ws, Y, X
 
     def ev_us(fn, iters):
