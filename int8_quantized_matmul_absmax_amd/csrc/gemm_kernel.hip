@@ -198,10 +198,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 
   // ---- outlier columns, 16 at a time: the recovered fp16 weight columns of
   // this block's BN features and the gathered fp16 activations of its BM
-  // tokens are staged in LDS for the epilogue. Chunk 0 is gathered in the
-  // prologue, between the stage loads, and held in registers until the main
-  // loop has freed LDS; further chunks (more than 16 outlier columns) are
-  // read in the epilogue.
+  // tokens are staged in LDS for the epilogue. Chunk 0 is held in registers
+  // until the main loop has freed LDS: its activations are read in the
+  // prologue, between the stage loads; its int8 weight codes are picked out
+  // of the stage buffers as the main loop streams Wq through LDS (the fp16
+  // weight's own values, with Wf given, are read in the prologue). Further
+  // chunks (more than 16 outlier columns) are read in the epilogue.
   const int n_o = (Xo && cols && n_out && Y) ? *n_out : 0;
   const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
   // More than 16 outlier columns with the recovered weights materialized (Wo
@@ -244,14 +246,33 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
         const uint32_t h = t < n_o ? (uint32_t)row[c] : 0u;
         keep[t / 2] |= h << (16 * (t % 2));
       }
-    } else {
-      const int8_t* row = Wq + (n0 + hr) * K;
+    }
+  };
+  // The int8 weight codes of chunk 0 come from the stage buffers: while the
+  // stage holding k-block kb (Wq[n0 .. n0+BN), columns kb*BK ..) is resident,
+  // thread BM + f reads its row's byte of every outlier column in it. A gather
+  // from Wq in memory instead would fetch a separate line for every (row,
+  // column) and hold up the prologue. The columns are ascending and the
+  // k-blocks come in order, so two uniform values track them: pt, the number
+  // picked so far, and pc, the next one's column (INT_MAX after the last),
+  // read with a scalar load as soon as the previous one is picked. A step
+  // without an outlier column costs one scalar compare.
+  const bool pick_w = !seg2 && Wf == nullptr && n_o > 0;
+  const int n_pick = pick_w ? min(n_o, 16) : 0;
+  int pt = 0;
+  int pc = n_pick > 0 ? cols[0] : INT_MAX;
+  auto pick_stage = [&](int kb) __attribute__((always_inline)) {
+    while (pc < (kb + 1) * BK) {
+      if (!tok_side) {
+        const int o = pc - kb * BK;   // byte in the row's k-block
+        const int8_t* row = stages + (kb % STAGES) * Cfg::STAGE_BYTES + hr * BK;
+        const uint32_t q = (uint8_t)row[(((o >> 4) ^ swz_key(hr)) << 4) + (o & 15)];
+        const uint32_t qs = q << (8 * (pt & 3));
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int c = t < n_o ? __builtin_amdgcn_readfirstlane(cols[t]) : 0;
-        const uint32_t q = t < n_o ? (uint8_t)row[c] : 0u;
-        keep[t / 4] |= q << (8 * (t % 4));
+        for (int i = 0; i < 4; ++i) keep[i] |= (pt >> 2) == i ? qs : 0u;
       }
+      ++pt;
+      pc = pt < n_pick ? cols[min(pt, n_pick - 1)] : INT_MAX;
     }
   };
   auto store_outliers = [&]() {
@@ -402,9 +423,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   static_assert(STAGES == 5, "the paired issue order is written for five stages");
   constexpr int RGROUPS = LOADS * 3 / 4;
   constexpr int MPG = Cfg::NMFMA / LOADS;
-  auto step = [&](int k, int set, auto f16) {
+  auto step = [&](int k, int set, auto f16) __attribute__((always_inline)) {
     if (set == 0) wait_vmcnt<2 * LOADS>(); else wait_vmcnt<LOADS + 1>();
     lds_barrier();
+    if constexpr (!decltype(f16)::value)
+      if (pick_w) pick_stage(k + 1);   // stage k+1 has landed and stays until step k+1
     const int8_t* rbase = stages + ((k + 1) % STAGES) * Cfg::STAGE_BYTES;
     const int pair0 = set == 0 ? k + 4 : k + 3;
     const int row_half = set == 0 ? 0 : LOADS / 2;
@@ -443,10 +466,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // stages 0 .. 3 have been issued (issue_pair(0), then issue_pair(2)); the
   // first wait leaves in flight the second pair and at most one load before
   // it (stage 1's last, or the last outlier gather), so stage 0 has landed.
-  auto run_steps = [&](int steps, auto f16) {
+  auto run_steps = [&](int steps, auto f16) __attribute__((always_inline)) {
     wait_vmcnt<2 * LOADS + 1>();
     lds_barrier();
     read_frags(0, 0);
+    if constexpr (!decltype(f16)::value)
+      if (pick_w) pick_stage(0);
     step(0, 0, f16);
     int k = 1;
     for (; k + 1 < steps; k += 2) {

@@ -516,3 +516,38 @@ def test_empty_k(gpu, M):
     assert not host(sx).view(np.uint32).any() and int(host(n)[0]) == 0
     assert np.array_equal(host(Ys).view(np.uint16), ref_bits)
     assert not host(C).any()
+
+
+@pytest.mark.parametrize("case", ["small_tiles", "large_tiles"])
+def test_outlier_columns_at_block_edges(gpu, case):
+    """The first 16 outlier columns' weight codes are taken from the GEMM's
+    staged k-blocks of 64 columns: columns sharing a k-block, on both sides
+    of a k-block boundary, column 0, and the last column of a partial last
+    k-block (K % 64 != 0); all 16 slots filled (small tiles) or 10 (large
+    tiles). Intermediates bit for bit, C bit for bit (int32 step call), Y
+    within the tolerance."""
+    note("outlier columns at block edges %s" % case)
+    rng = np.random.default_rng(900 + len(case))
+    if case == "small_tiles":
+        M, K, N = 300, 1040, 260
+        cols = [0, 1, 15, 16, 63, 64, 65, 127, 128, 500, 511, 512, 1000, 1023, 1024, 1039]
+    else:
+        M, K, N = 4100, 528, 4100
+        cols = [0, 1, 63, 64, 255, 256, 511, 512, 520, 527]
+    X = np.clip(synth.normal_f16(rng, (M, K), 1.0).astype(np.float32), -5.0, 5.0).astype(np.float16)
+    for c in cols:
+        rows = rng.choice(M, size=max(1, M // 8), replace=False)
+        X[rows, c] = (rng.uniform(7.0, 30.0, rows.size) * rng.choice([-1.0, 1.0], rows.size)).astype(np.float16)
+    W = synth.normal_f16(rng, (N, K), 0.05)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0)
+    assert ref["cols"].tolist() == cols
+    Y, views = _run_linear(gpu, X, Wq, sw, 6.0)
+    _check_intermediates(gpu, views, X, ref)
+    assert y_err(Y, ref["Y"]) <= Y_TOL
+    ops = _ops(gpu)
+    Y2, C = ops.int8_mm_dequant(views["Xq"], dev(Wq), views["sx"], dev(sw), views["Xo"],
+                                views["cols"], views["n"], want_int32=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(C), O.int32_accumulators(ref["Xq"], Wq))
+    assert np.array_equal(host(Y2).view(np.uint16), Y.view(np.uint16))
