@@ -1,9 +1,13 @@
 // Bandwidth-bound kernels of the LLM.int8() layer on gfx950:
-//   - outlier-column detection (column OR-reduce of abs(x) >= threshold),
+//   - outlier-column detection (column OR-reduce of abs(x) >= threshold):
+//     atomically into a cleared bitmap for the step call, or as per-row-band
+//     partial words with plain stores for the layer,
 //   - bitmap -> ascending outlier-column list,
 //   - per-row absmax int8 quantization (of X rows over the non-outlier
 //     columns, or of W rows over the full row) fused with the gather of the
 //     outlier columns of X,
+//   - the fp16 outlier weight columns Wo for the GEMM's second segment
+//     (recovered from the int8 weight, or the fp16 weight's own columns),
 //   - exact-erf GELU for MLP blocks built from the layer.
 //
 // Pages cited: [HF-blog] Hugging Face blog "A Gentle Introduction to 8-bit
