@@ -444,6 +444,10 @@ def test_gelu(gpu):
     note("gelu")
     rng = np.random.default_rng(8)
     X = synth.normal_f16(rng, (4099,), 3.0)
+    # signed zero, the fp16 extremes and large magnitudes, in the 8-element
+    # groups and in the partial last group (4099 = 512 * 8 + 3)
+    X[[0, 1, 2, 3, 4096, 4097, 4098]] = np.array(
+        [-0.0, 65504.0, -65504.0, -20.0, 20.0, -9.5, 1e-7], np.float32).astype(np.float16)
     Y = host(_ops(gpu).gelu_f16(dev(X)))
     ref = O.gelu_erf(X.astype(np.float64))
     ref16 = ref.astype(np.float16)
