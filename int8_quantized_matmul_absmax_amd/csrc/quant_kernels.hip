@@ -479,8 +479,15 @@ __global__ __launch_bounds__(kWoThreads) void k_recover_outlier_w(
   auto codes = [&](int64_t j, int64_t t0, int c[8], int q[8]) {
     load_cols8(cols, t0, n, c);
     const int8_t* row = Wq + j * K;
+    if (c[0] >= 0 && c[7] == c[0] + 7 && (c[0] & 7) == 0) {
+      // 8 consecutive columns (they ascend) from a multiple of 8: one load
+      const uint2 v = *reinterpret_cast<const uint2*>(row + c[0]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = c[e] >= 0 ? (int)row[c[e]] : 0;
+      for (int e = 0; e < 8; ++e) q[e] = (int)(int8_t)((e < 4 ? v.x : v.y) >> (8 * (e & 3)));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = c[e] >= 0 ? (int)row[c[e]] : 0;
+    }
   };
   auto store = [&](int64_t j, int64_t t0, const uint32_t h[8]) {
     st16(Wo + j * ld + t0, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
@@ -536,6 +543,10 @@ __global__ __launch_bounds__(kWoThreads) void k_gather_w_cols(
     int c[8];
     load_cols8(cols, t0, n, c);
     const uint16_t* row = W + j * K;
+    if (c[0] >= 0 && c[7] == c[0] + 7 && (c[0] & 7) == 0) {
+      st16(Wo + j * ld + t0, ld16(row + c[0]));   // 8 consecutive columns: one load
+      return;
+    }
     uint32_t h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = c[e] >= 0 ? (uint32_t)row[c[e]] : 0u;
