@@ -100,10 +100,10 @@ __device__ __forceinline__ uint2 codes8_rne(const uint4& t, float s) {
 }
 
 // Workgroup barrier for data exchanged through LDS only: this wave's LDS
-// operations complete (lgkmcnt(0), gfx9 encoding), then s_barrier. Global
-// loads stay in flight across it; __syncthreads' fence would wait for them.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
+// operations complete (lgkmcnt(0), gfx9 encoding), then s_barrier, with no
+// fence on global memory, so nothing in flight there is waited for. The
+// empty asm statements keep the compiler from moving memory accesses across
+// the barrier.
 __device__ __forceinline__ void lds_only_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -122,7 +122,7 @@ constexpr int kBlockThreads = 256;
 
 // Exclusive prefix of popcount over the bitmap words, in LDS. Returns the
 // total (the outlier count n). All threads of the block must call it.
-// kLdsOnly: its barriers leave the caller's global loads in flight.
+// kLdsOnly: its barriers order LDS only (no fence on global memory).
 template <bool kLdsOnly = false>
 __device__ inline int bitmap_prefix(const uint32_t* sbm, uint32_t* spre, int nwords, int* sred) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
