@@ -45,10 +45,14 @@
 // spread over the MFMA phase instead of bursting after each barrier.
 //
 // LDS layout of one stage: rows of BK = 64 bytes (Wq rows first, then Xq
-// rows); 16-byte chunk c of row r sits at position c ^ f(r),
-// f(r) = ((r >> 1) ^ (r >> 3)) & 3, so fragment reads of 8 (or 16)
-// consecutive rows at one logical chunk hit distinct 16-byte bank groups of a
-// 128-byte (or 256-byte) bank window.
+// rows); 16-byte chunk c of row r sits at position c ^ f(r), f(r) =
+// (r >> 2) & 3. A fragment read (lane l < 32 at row l, lane l + 32 at the
+// same row, next chunk) then completes in the minimum number of LDS cycles;
+// the bank-conflict counter reads zero for it, as it does for 16-byte reads
+// of consecutive addresses. Measured alternatives: with no swizzle such a
+// read takes 3.9x the cycles; with f(r) = ((r >> 1) ^ (r >> 3)) & 3 it takes
+// 1.95x. The layout only permutes which chunk each lane's DMA load fetches:
+// every row is still read as one 64-byte segment and written to LDS in order.
 //
 // Epilogue: per-tile dequantization with the row / column factors staged in
 // LDS; the fp16 outlier product (first 16 outlier columns: gathered in the
@@ -110,7 +114,7 @@ struct GemmCfg {
   static_assert(NMFMA % LOADS == 0 && NREADS % LOADS == 0, "interleave");
 };
 
-__device__ __forceinline__ int swz_key(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_key(int r) { return (r >> 2) & 3; }
 
 // Buffer descriptor over [base, base + bytes); reads past `bytes` return 0.
 // The fields go through readfirstlane so the descriptor lives in SGPRs (the
