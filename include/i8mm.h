@@ -186,6 +186,34 @@ I8MM_API int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx
                     const uint16_t* bias, uint16_t* Y, int32_t* C, i8mm_stream_t stream);
 
 /*
+ * outlier_detect_quantize  (steps: outlier-column detection, X-side split and
+ * row-wise quantization of the normal part, fused as the layer runs them)
+ *
+ * [Summary] "The full picture" steps 1-3 on the activation side: find the
+ * outlier feature dimensions, split X along them, quantize the normal part
+ * row-wise ([HF-blog] "Inside the MatMul"). It performs exactly the
+ * activation side of linear_int8_mixed (the same two kernel launches, one
+ * read of X for detection and one for the row pass) and leaves its results
+ * in the workspace, where int8_mm_dequant can take them: a caller that runs
+ * the matmul itself, or times the two sides apart.
+ *
+ *   X          fp16 [M, K], read only.
+ *   threshold  host float, as in outlier_detect_gather.
+ *   workspace  as in linear_int8_mixed (at least
+ *              linear_int8_mixed_workspace_bytes(M, K) bytes, 256-byte
+ *              aligned). Written, at the offsets i8mm_workspace_layout
+ *              reports: the bitmap, cols and n as outlier_detect_gather
+ *              writes them; sx and Xq as int8_quantize_rowwise writes them
+ *              given that bitmap; Xo [M, I8MM_OUTLIER_LD(n)] with zero pads.
+ *
+ * M == 0 does nothing. Errors: EINVAL, EALIGN, EWORKSPACE, ERANGE,
+ * ENODEVICE, ELAUNCH.
+ */
+I8MM_API int outlier_detect_quantize(const uint16_t* X, int64_t M, int64_t K, float threshold,
+                                     void* workspace, size_t workspace_bytes,
+                                     i8mm_stream_t stream);
+
+/*
  * linear_int8_mixed  (the whole layer for an already-quantized weight)
  *
  * [HF-blog] "A gentle summary of LLM.int8()" steps 1-3 and "Inside the
@@ -201,7 +229,7 @@ I8MM_API int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx
  *   workspace  device buffer of at least linear_int8_mixed_workspace_bytes(M,K)
  *              bytes, 256-byte aligned; it receives the intermediates (outlier
  *              bitmap, cols, n, sx, Xq, Xo) at the offsets that
- *              i8mm_workspace_offsets reports. Given at least
+ *              i8mm_workspace_layout reports. Given at least
  *              linear_int8_mixed_workspace_bytes_many_outliers(M, K, N) bytes,
  *              the recovered outlier weight columns go after them (see that
  *              call) and many outlier columns take the fast path.
@@ -277,7 +305,7 @@ I8MM_API size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64
  * partial flag words, 16 x ceil(K/32) uint32 at most), whose contents on
  * entry do not matter.
  * `offsets` is a host array of 7 int64. Errors: EINVAL. */
-I8MM_API int i8mm_workspace_offsets(int64_t M, int64_t K, int64_t* offsets);
+I8MM_API int i8mm_workspace_layout(int64_t M, int64_t K, int64_t* offsets);
 
 /*
  * i8mm_gelu_f16: exact-erf GELU, y = fp16(x * erfc(-x / sqrt 2) / 2) (equal to

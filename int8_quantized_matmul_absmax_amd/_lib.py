@@ -20,12 +20,13 @@ EXPORTS = (
     "int8_quantize_colwise_weight",
     "int8_quantize_rowwise",
     "outlier_detect_gather",
+    "outlier_detect_quantize",
     "int8_mm_dequant",
     "linear_int8_mixed",
     "linear_int8_mixed_fp16_weights",
     "linear_int8_mixed_workspace_bytes",
     "linear_int8_mixed_workspace_bytes_many_outliers",
-    "i8mm_workspace_offsets",
+    "i8mm_workspace_layout",
     "i8mm_gelu_f16",
     "i8mm_last_error",
     "i8mm_status_string",
@@ -53,6 +54,7 @@ def _declare(lib):
         "int8_quantize_colwise_weight": ([vp, i64, i64, vp, vp, vp], i32),
         "int8_quantize_rowwise": ([vp, i64, i64, vp, vp, vp, vp], i32),
         "outlier_detect_gather": ([vp, i64, i64, f32, vp, vp, vp, vp, vp], i32),
+        "outlier_detect_quantize": ([vp, i64, i64, f32, vp, ctypes.c_size_t, vp], i32),
         "int8_mm_dequant": ([vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "linear_int8_mixed": ([vp, i64, i64, vp, vp, i64, vp, f32, vp, vp, ctypes.c_size_t, vp],
                               i32),
@@ -60,7 +62,7 @@ def _declare(lib):
                                             ctypes.c_size_t, vp], i32),
         "linear_int8_mixed_workspace_bytes": ([i64, i64], ctypes.c_size_t),
         "linear_int8_mixed_workspace_bytes_many_outliers": ([i64, i64, i64], ctypes.c_size_t),
-        "i8mm_workspace_offsets": ([i64, i64, ctypes.POINTER(ctypes.c_int64)], i32),
+        "i8mm_workspace_layout": ([i64, i64, ctypes.POINTER(ctypes.c_int64)], i32),
         "i8mm_gelu_f16": ([vp, i64, vp, vp], i32),
         "i8mm_last_error": ([], ctypes.c_char_p),
         "i8mm_status_string": ([i32], ctypes.c_char_p),

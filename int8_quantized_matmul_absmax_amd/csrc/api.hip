@@ -137,9 +137,9 @@ size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64_t K, int
   return (size_t)(off[6] + wo_region_bytes(N, K));
 }
 
-int i8mm_workspace_offsets(int64_t M, int64_t K, int64_t* offsets) {
-  if (!offsets) return fail(I8MM_EINVAL, "i8mm_workspace_offsets: offsets is NULL");
-  if (!layout(M, K, offsets)) return fail(I8MM_EINVAL, "i8mm_workspace_offsets: invalid sizes");
+int i8mm_workspace_layout(int64_t M, int64_t K, int64_t* offsets) {
+  if (!offsets) return fail(I8MM_EINVAL, "i8mm_workspace_layout: offsets is NULL");
+  if (!layout(M, K, offsets)) return fail(I8MM_EINVAL, "i8mm_workspace_layout: invalid sizes");
   return ok();
 }
 
@@ -231,6 +231,38 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
 
 namespace {
 
+// The activation side of the layer (steps a1-a3) into the workspace:
+// detection as per-band partial flags (no clearing launch), then the row
+// pass, which ORs them, writes the bitmap, cols and n, gathers the outlier
+// columns into Xo and quantizes the normal part into Xq, sx.
+int x_side(const char* fn, const uint16_t* X, int64_t M, int64_t K, uint32_t tau16, char* ws,
+           const int64_t* off, int64_t off_part, hipStream_t s) {
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + off[0]);
+  int32_t* cols = reinterpret_cast<int32_t*>(ws + off[1]);
+  int32_t* n_o = reinterpret_cast<int32_t*>(ws + off[2]);
+  float* sx = reinterpret_cast<float*>(ws + off[3]);
+  int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
+  uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + off_part);
+  const int bands = i8mm::flag_bands(M, K);
+  I8MM_TRY(launched(i8mm::launch_outlier_flag_bands(X, M, K, tau16, bands, part, s), fn));
+  I8MM_TRY(launched(
+      i8mm::launch_rows_banded(X, M, K, part, bands, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+  return I8MM_OK;
+}
+
+// Workspace pointer and size checks shared by the calls that take one.
+int check_workspace(const char* fn, const void* workspace, size_t workspace_bytes,
+                    const int64_t* off) {
+  if (!workspace) return fail(I8MM_EWORKSPACE, "%s: workspace is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(I8MM_EALIGN, "%s: workspace is not 256-byte aligned", fn);
+  if ((int64_t)workspace_bytes < off[6])
+    return fail(I8MM_EWORKSPACE, "%s: workspace has %zu bytes, needs %lld", fn, workspace_bytes,
+                (long long)off[6]);
+  return I8MM_OK;
+}
+
 // The whole layer after argument checks common to both weight modes. Wf: the
 // fp16 weight when the layer keeps one (its outlier columns feed the outlier
 // product), else nullptr (they are recovered from Wq, sw). quantize_w: write
@@ -248,12 +280,7 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
   I8MM_TRY(check_ptr(fn, "Y", Y, M * N > 0));
   int64_t off[7], off_part = 0;
   layout(M, K, off, &off_part);
-  if (!workspace) return fail(I8MM_EWORKSPACE, "%s: workspace is NULL", fn);
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
-    return fail(I8MM_EALIGN, "%s: workspace is not 256-byte aligned", fn);
-  if ((int64_t)workspace_bytes < off[6])
-    return fail(I8MM_EWORKSPACE, "%s: workspace has %zu bytes, needs %lld", fn, workspace_bytes,
-                (long long)off[6]);
+  I8MM_TRY(check_workspace(fn, workspace, workspace_bytes, off));
   if (M == 0 || N == 0) return ok();
   I8MM_TRY(check_device());
   char* ws = static_cast<char*>(workspace);
@@ -275,13 +302,7 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
                       fn));
     return ok();
   }
-  // detection as per-band partial flags (no clearing launch), then the row
-  // pass, which ORs them and also writes the bitmap, cols and n
-  uint32_t* part = reinterpret_cast<uint32_t*>(ws + off_part);
-  const int bands = i8mm::flag_bands(M, K);
-  I8MM_TRY(launched(i8mm::launch_outlier_flag_bands(X, M, K, tau16, bands, part, s), fn));
-  I8MM_TRY(launched(
-      i8mm::launch_rows_banded(X, M, K, part, bands, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+  I8MM_TRY(x_side(fn, X, M, K, tau16, ws, off, off_part, s));
   // With room for it, the fp16 outlier weight columns are materialized for
   // the tiled GEMM (the kernels do nothing for 16 or fewer columns).
   uint16_t* Wo = nullptr;
@@ -317,6 +338,22 @@ int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_t K, cons
   I8MM_TRY(check_ptr(fn, "W", W, N * K > 0));
   return run_layer(fn, X, M, K, Wq, sw, N, bias, threshold, Y, workspace, workspace_bytes,
                    (hipStream_t)stream, W, quantize_weight != 0);
+}
+
+int outlier_detect_quantize(const uint16_t* X, int64_t M, int64_t K, float threshold,
+                            void* workspace, size_t workspace_bytes, i8mm_stream_t stream) {
+  const char* fn = "outlier_detect_quantize";
+  I8MM_TRY(check_dims(fn, M, 0, K));
+  if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
+  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
+  int64_t off[7], off_part = 0;
+  layout(M, K, off, &off_part);
+  I8MM_TRY(check_workspace(fn, workspace, workspace_bytes, off));
+  if (M == 0) return ok();
+  I8MM_TRY(check_device());
+  I8MM_TRY(x_side(fn, X, M, K, i8mm::fp16_threshold_pattern(threshold),
+                  static_cast<char*>(workspace), off, off_part, (hipStream_t)stream));
+  return ok();
 }
 
 int i8mm_gelu_f16(const uint16_t* X, int64_t count, uint16_t* Y, i8mm_stream_t stream) {

@@ -37,6 +37,7 @@
 // the 16 token rows of one read hit distinct banks), partial tiles summed
 // through LDS.
 
+#include <atomic>
 #include <algorithm>
 
 #include "device_common.h"
@@ -375,7 +376,11 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   }
 }
 
-int g_cus = 0;
+// One-time per-device state of the launcher. Concurrent first calls from
+// several host threads may both set it; the values are the same, and the
+// atomics make that benign.
+constexpr int kDcMaxDevices = 64;
+std::atomic<int> g_cus[kDcMaxDevices];
 
 template <int MR, int JC>
 hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw, int64_t M,
@@ -383,26 +388,30 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
                            uint16_t* Y, const uint16_t* Wf, uint32_t* bitmap, int32_t* cols,
                            int32_t* n_out, float* sx, int8_t* Xq, uint16_t* Xo, hipStream_t s) {
   const int lds = dc_lds_bytes((int)M, (int)K);
-  static bool lds_set = false;   // per instantiation: allow the largest dynamic LDS once
-  if (!lds_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_i8<MR, JC>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             dc_lds_bytes(MR, JC * kDcThreads * 8));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int slot = dev >= 0 && dev < kDcMaxDevices ? dev : 0;
+  // per instantiation and device: allow the largest dynamic LDS once
+  static std::atomic<bool> lds_set[kDcMaxDevices];
+  if (!lds_set[slot].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_i8<MR, JC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            dc_lds_bytes(MR, JC * kDcThreads * 8));
     if (e != hipSuccess) return e;
-    lds_set = true;
+    lds_set[slot].store(true, std::memory_order_release);
   }
-  if (g_cus == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  int cus = g_cus[slot].load(std::memory_order_acquire);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    g_cus = cus;
+    g_cus[slot].store(cus, std::memory_order_release);
   }
   // two blocks per CU while both fit in LDS (static part about 7.5 KiB)
   const int64_t per_cu = lds + 8 * 1024 <= 80 * 1024 ? 2 : 1;
   const int64_t tiles = (N + kDcFeat - 1) / kDcFeat;
-  const int64_t blocks = std::min<int64_t>(tiles, per_cu * g_cus);
+  const int64_t blocks = std::min<int64_t>(tiles, per_cu * cus);
   hipLaunchKernelGGL((k_decode_i8<MR, JC>), dim3((unsigned)blocks), dim3(kDcThreads), (size_t)lds, s, X,
                      Wq, sw, (int)M, (int)N, (int)K, tau16, bias, Y, Wf, bitmap, cols, n_out, sx,
                      Xq, Xo);

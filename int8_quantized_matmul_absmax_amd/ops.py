@@ -34,17 +34,37 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, ndim=None):
+def _need(t, name, dtype, ndim=None, shape=None, min_numel=None):
+    """Type, dtype, contiguity and size of one tensor argument (no device check:
+    _on_gpu does that for all arguments of a call together)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if not t.is_cuda:
-        raise ValueError("%s must be on a GPU (the path runs on the GPU only)" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if ndim is not None and t.dim() != ndim:
         raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s must hold at least %d elements, got %d" % (name, min_numel, t.numel()))
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None = absent) is on one GPU; returns that device.
+    The path runs on the GPU only: a host tensor is an error, not a fallback."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be on a GPU (the path runs on the GPU only)" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
+    return dev
 
 
 def _flatten_tokens(X):
@@ -59,12 +79,15 @@ def int8_quantize_colwise_weight(W, Wq=None, sw=None):
     lib = _lib.load_library()
     _need(W, "W", torch.float16, 2)
     N, K = W.shape
-    Wq = Wq if Wq is not None else torch.empty((N, K), dtype=torch.int8, device=W.device)
-    sw = sw if sw is not None else torch.empty((N,), dtype=torch.float32, device=W.device)
-    _need(Wq, "Wq", torch.int8, 2)
-    _need(sw, "sw", torch.float32, 1)
+    if Wq is not None:
+        _need(Wq, "Wq", torch.int8, shape=(N, K))
+    if sw is not None:
+        _need(sw, "sw", torch.float32, shape=(N,))
+    dev = _on_gpu(W=W, Wq=Wq, sw=sw)
+    Wq = Wq if Wq is not None else torch.empty((N, K), dtype=torch.int8, device=dev)
+    sw = sw if sw is not None else torch.empty((N,), dtype=torch.float32, device=dev)
     _lib.check(lib.int8_quantize_colwise_weight(_ptr(W), N, K, _ptr(Wq), _ptr(sw),
-                                                _stream(W.device)))
+                                                _stream(dev)))
     return Wq, sw
 
 
@@ -76,13 +99,16 @@ def int8_quantize_rowwise(X, outlier_bitmap=None, Xq=None, sx=None):
     X2 = _flatten_tokens(X)
     M, K = X2.shape
     if outlier_bitmap is not None:
-        _need(outlier_bitmap, "outlier_bitmap", torch.int32, 1)
-        if outlier_bitmap.numel() < (K + 31) // 32:
-            raise ValueError("outlier_bitmap too small")
-    Xq = Xq if Xq is not None else torch.empty((M, K), dtype=torch.int8, device=X.device)
-    sx = sx if sx is not None else torch.empty((M,), dtype=torch.float32, device=X.device)
+        _need(outlier_bitmap, "outlier_bitmap", torch.int32, 1, min_numel=(K + 31) // 32)
+    if Xq is not None:
+        _need(Xq, "Xq", torch.int8, shape=(M, K))
+    if sx is not None:
+        _need(sx, "sx", torch.float32, shape=(M,))
+    dev = _on_gpu(X=X, outlier_bitmap=outlier_bitmap, Xq=Xq, sx=sx)
+    Xq = Xq if Xq is not None else torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = sx if sx is not None else torch.empty((M,), dtype=torch.float32, device=dev)
     _lib.check(lib.int8_quantize_rowwise(_ptr(X2), M, K, _ptr(outlier_bitmap), _ptr(Xq), _ptr(sx),
-                                         _stream(X.device)))
+                                         _stream(dev)))
     return Xq, sx
 
 
@@ -98,7 +124,7 @@ def outlier_detect_gather(X, threshold=DEFAULT_THRESHOLD, gather=True):
     _need(X, "X", torch.float16)
     X2 = _flatten_tokens(X)
     M, K = X2.shape
-    dev = X.device
+    dev = _on_gpu(X=X)
     bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=dev)
     cols = torch.empty((max(K, 1),), dtype=torch.int32, device=dev)
     n = torch.empty((1,), dtype=torch.int32, device=dev)
@@ -108,25 +134,59 @@ def outlier_detect_gather(X, threshold=DEFAULT_THRESHOLD, gather=True):
     return bitmap, cols, n, Xo
 
 
+def outlier_detect_quantize(X, threshold=DEFAULT_THRESHOLD, workspace=None):
+    """The activation side of linear_int8_mixed alone (detection, gather and
+    row quantization, the same two kernels) into a layer workspace. Returns
+    the workspace; workspace_views(workspace, M, K) gives bitmap, cols, n, sx,
+    Xq and Xo, which int8_mm_dequant takes."""
+    lib = _lib.load_library()
+    _need(X, "X", torch.float16)
+    X2 = _flatten_tokens(X)
+    M, K = X2.shape
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, min_numel=workspace_bytes(M, K))
+    dev = _on_gpu(X=X, workspace=workspace)
+    if workspace is None:
+        workspace = torch.empty((max(workspace_bytes(M, K), 1),), dtype=torch.uint8, device=dev)
+    _lib.check(lib.outlier_detect_quantize(_ptr(X2), M, K, float(threshold), _ptr(workspace),
+                                           workspace.numel(), _stream(dev)))
+    return workspace
+
+
 def int8_mm_dequant(Xq, Wq, sx, sw, Xo=None, cols=None, n=None, bias=None, want_y=True,
-                    want_int32=False):
+                    want_int32=False, out=None):
     """int8 GEMM (int32 accumulation) with the fused dequantization, fp16 outlier
-    product and bias. Returns Y fp16 [M, N] and/or C int32 [M, N]."""
+    product and bias. Returns Y fp16 [M, N] and/or C int32 [M, N].
+
+    Xo, cols, n come together (from outlier_detect_gather or a layer
+    workspace): Xo fp16 of capacity >= M * outlier_ld(K) (the count n is only
+    known on the device, so room for every column is required), cols int32
+    with >= K entries, n int32 [1] on the device."""
     lib = _lib.load_library()
     _need(Xq, "Xq", torch.int8, 2)
-    _need(Wq, "Wq", torch.int8, 2)
-    _need(sx, "sx", torch.float32, 1)
-    _need(sw, "sw", torch.float32, 1)
     M, K = Xq.shape
+    _need(Wq, "Wq", torch.int8, 2)
     N = Wq.shape[0]
-    if Wq.shape[1] != K or sx.numel() != M or sw.numel() != N:
-        raise ValueError("shape mismatch")
+    _need(Wq, "Wq", torch.int8, shape=(N, K))
+    _need(sx, "sx", torch.float32, shape=(M,))
+    _need(sw, "sw", torch.float32, shape=(N,))
+    given = [t is not None for t in (Xo, cols, n)]
+    if any(given) and not all(given):
+        raise ValueError("Xo, cols and n must be given together")
+    if Xo is not None:
+        _need(Xo, "Xo", torch.float16, min_numel=M * outlier_ld(K))
+        _need(cols, "cols", torch.int32, min_numel=K)
+        _need(n, "n", torch.int32, shape=(1,))
     if bias is not None:
-        _need(bias, "bias", torch.float16, 1)
-        if bias.numel() != N:
-            raise ValueError("bias must have N entries")
-    dev = Xq.device
-    Y = torch.empty((M, N), dtype=torch.float16, device=dev) if want_y else None
+        _need(bias, "bias", torch.float16, shape=(N,))
+    if out is not None:
+        _need(out, "out", torch.float16, shape=(M, N))
+    if not (want_y or want_int32):
+        raise ValueError("nothing requested: want_y and want_int32 are both False")
+    dev = _on_gpu(Xq=Xq, Wq=Wq, sx=sx, sw=sw, Xo=Xo, cols=cols, n=n, bias=bias, out=out)
+    Y = None
+    if want_y:
+        Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
     C = torch.empty((M, N), dtype=torch.int32, device=dev) if want_int32 else None
     _lib.check(lib.int8_mm_dequant(_ptr(Xq), _ptr(Wq), _ptr(sx), _ptr(sw), M, N, K, _ptr(Xo),
                                    _ptr(cols), _ptr(n), _ptr(bias), _ptr(Y), _ptr(C),
@@ -146,38 +206,48 @@ def workspace_bytes(M, K, N=None):
     return int(lib.linear_int8_mixed_workspace_bytes_many_outliers(int(M), int(K), int(N)))
 
 
-def workspace_offsets(M, K):
+def workspace_layout(M, K):
     """Byte offsets of bitmap, cols, n, sx, Xq, Xo in the workspace, and its size."""
     lib = _lib.load_library()
     off = (ctypes.c_int64 * 7)()
-    _lib.check(lib.i8mm_workspace_offsets(int(M), int(K), off))
+    _lib.check(lib.i8mm_workspace_layout(int(M), int(K), off))
     keys = ("bitmap", "cols", "n", "sx", "Xq", "Xo", "total")
     return dict(zip(keys, [int(v) for v in off]))
 
 
-def linear_int8_mixed(X, Wq, sw, bias=None, threshold=DEFAULT_THRESHOLD, workspace=None, out=None):
-    """The whole layer: Y = X . W^T with outlier decomposition, for an int8 weight
-    (Wq, sw) from int8_quantize_colwise_weight. X [..., K] fp16 -> Y [..., N] fp16."""
-    lib = _lib.load_library()
-    _need(X, "X", torch.float16)
-    _need(Wq, "Wq", torch.int8, 2)
-    _need(sw, "sw", torch.float32, 1)
+def _layer_buffers(X, N, bias, workspace, out, K_w, W_name):
+    """Shared argument checks of the two layer calls; returns (X2, M, K, dev,
+    workspace, Y, lead)."""
     lead = X.shape[:-1]
     X2 = _flatten_tokens(X)
     M, K = X2.shape
-    N = Wq.shape[0]
-    if Wq.shape[1] != K or sw.numel() != N:
-        raise ValueError("shape mismatch")
+    if K_w != K:
+        raise ValueError("%s has %d input features, X has %d" % (W_name, K_w, K))
     if bias is not None:
-        _need(bias, "bias", torch.float16, 1)
-    dev = X.device
+        _need(bias, "bias", torch.float16, shape=(N,))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, min_numel=workspace_bytes(M, K))
+    if out is not None:
+        _need(out, "out", torch.float16)
+        if out.numel() != M * N:
+            raise ValueError("out must hold M * N = %d elements, got %d" % (M * N, out.numel()))
+    return X2, M, K, lead
+
+
+def linear_int8_mixed(X, Wq, sw, bias=None, threshold=DEFAULT_THRESHOLD, workspace=None, out=None):
+    """The whole layer: Y = X . W^T with outlier decomposition, for an int8 weight
+    (Wq, sw) from int8_quantize_colwise_weight. X [..., K] fp16 -> Y [..., N] fp16.
+    Without a workspace, one of workspace_bytes(M, K, N) bytes is allocated."""
+    lib = _lib.load_library()
+    _need(X, "X", torch.float16)
+    _need(Wq, "Wq", torch.int8, 2)
+    N = Wq.shape[0]
+    _need(sw, "sw", torch.float32, shape=(N,))
+    X2, M, K, lead = _layer_buffers(X, N, bias, workspace, out, Wq.shape[1], "Wq")
+    dev = _on_gpu(X=X, Wq=Wq, sw=sw, bias=bias, workspace=workspace, out=out)
     if workspace is None:
-        need = workspace_bytes(M, K, N)
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    else:
-        _need(workspace, "workspace", torch.uint8, 1)
+        workspace = torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
-    _need(Y, "out", torch.float16)
     _lib.check(lib.linear_int8_mixed(_ptr(X2), M, K, _ptr(Wq), _ptr(sw), N, _ptr(bias),
                                      float(threshold), _ptr(Y), _ptr(workspace),
                                      workspace.numel(), _stream(dev)))
@@ -193,24 +263,14 @@ def linear_int8_mixed_fp16_weights(X, W, Wq, sw, quantize_weight=True, bias=None
     lib = _lib.load_library()
     _need(X, "X", torch.float16)
     _need(W, "W", torch.float16, 2)
-    _need(Wq, "Wq", torch.int8, 2)
-    _need(sw, "sw", torch.float32, 1)
-    lead = X.shape[:-1]
-    X2 = _flatten_tokens(X)
-    M, K = X2.shape
-    N = W.shape[0]
-    if W.shape[1] != K or tuple(Wq.shape) != (N, K) or sw.numel() != N:
-        raise ValueError("shape mismatch")
-    if bias is not None:
-        _need(bias, "bias", torch.float16, 1)
-    dev = X.device
+    N, K_w = W.shape
+    _need(Wq, "Wq", torch.int8, shape=(N, K_w))
+    _need(sw, "sw", torch.float32, shape=(N,))
+    X2, M, K, lead = _layer_buffers(X, N, bias, workspace, out, K_w, "W")
+    dev = _on_gpu(X=X, W=W, Wq=Wq, sw=sw, bias=bias, workspace=workspace, out=out)
     if workspace is None:
-        need = workspace_bytes(M, K, N)
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    else:
-        _need(workspace, "workspace", torch.uint8, 1)
+        workspace = torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
-    _need(Y, "out", torch.float16)
     _lib.check(lib.linear_int8_mixed_fp16_weights(
         _ptr(X2), M, K, _ptr(W), N, _ptr(Wq), _ptr(sw), 1 if quantize_weight else 0, _ptr(bias),
         float(threshold), _ptr(Y), _ptr(workspace), workspace.numel(), _stream(dev)))
@@ -221,8 +281,11 @@ def gelu_f16(X, out=None):
     """Exact-erf GELU in fp32 on an fp16 tensor (glue between MLP layers)."""
     lib = _lib.load_library()
     _need(X, "X", torch.float16)
+    if out is not None:
+        _need(out, "out", torch.float16, min_numel=X.numel())
+    dev = _on_gpu(X=X, out=out)
     Y = out if out is not None else torch.empty_like(X)
-    _lib.check(lib.i8mm_gelu_f16(_ptr(X), X.numel(), _ptr(Y), _stream(X.device)))
+    _lib.check(lib.i8mm_gelu_f16(_ptr(X), X.numel(), _ptr(Y), _stream(dev)))
     return Y
 
 
@@ -232,7 +295,7 @@ def workspace_views(workspace, M, K, N=None):
     outlier weight columns the tiled path materializes with more than 16
     outlier columns, N rows outlier_ld(n) halfs apart (flat, capacity
     N * outlier_ld(K))."""
-    off = workspace_offsets(M, K)
+    off = workspace_layout(M, K)
     w = workspace
     views = {
         "bitmap": w[off["bitmap"]:off["bitmap"] + ((K + 31) // 32) * 4].view(torch.int32),

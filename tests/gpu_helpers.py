@@ -30,6 +30,14 @@ def bitmap_u32(t):
     return host(t).view(np.uint32)
 
 
+def f16_ulp(a):
+    """The fp16 ulp of each value of a (float16 array): the spacing of its
+    binade. Finite at the largest finite fp16 (65504 lies in the binade
+    [32768, 65536), whose ulp is 32), where np.spacing overflows to inf."""
+    a16 = np.abs(np.asarray(a, np.float16))
+    return np.spacing(np.minimum(a16, np.float16(32768.0))).astype(np.float64)
+
+
 def y_err(Y_gpu, Y_ref):
     return O.max_abs_rel_error(np.asarray(Y_gpu, np.float64), Y_ref)
 

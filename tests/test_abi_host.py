@@ -59,7 +59,7 @@ def test_status_strings(lib):
 def test_workspace_layout_is_pure_and_consistent(lib):
     for M, K in [(1, 16), (16, 256), (2048, 4096), (4096, 12288), (0, 64)]:
         off = (ctypes.c_int64 * 7)()
-        assert lib.i8mm_workspace_offsets(M, K, off) == 0
+        assert lib.i8mm_workspace_layout(M, K, off) == 0
         off = list(off)
         assert off[0] == 0 and all(b >= a for a, b in zip(off, off[1:]))
         assert all(o % 256 == 0 for o in off)
@@ -71,7 +71,7 @@ def test_workspace_layout_is_pure_and_consistent(lib):
         assert lib.linear_int8_mixed_workspace_bytes(M, K) == off[6]
     assert lib.linear_int8_mixed_workspace_bytes(4, 20) == 0
     assert lib.linear_int8_mixed_workspace_bytes(-1, 16) == 0
-    assert lib.i8mm_workspace_offsets(4, 16, None) == _lib.I8MM_EINVAL
+    assert lib.i8mm_workspace_layout(4, 16, None) == _lib.I8MM_EINVAL
 
 
 def test_validation_quantize_weight(lib):
@@ -204,6 +204,67 @@ def test_python_ops_refuse_cpu_tensors():
         i8.ops.int8_quantize_colwise_weight(W)
     with pytest.raises(TypeError):
         i8.ops.int8_quantize_colwise_weight(W.float())
+
+
+def test_python_ops_check_every_size_before_launch():
+    """Every tensor a caller hands to the binding is checked for dtype and size
+    on the host, before anything reaches the library: a too-small output,
+    bias, scale vector, outlier buffer or count would otherwise become device
+    writes or reads out of bounds. Host tensors of the right sizes reach the
+    device check and stop there (the path runs on the GPU only)."""
+    import torch
+    ops = i8.ops
+    M, K, N = 8, 64, 32
+    f16, i8t, f32, i32 = torch.float16, torch.int8, torch.float32, torch.int32
+    X = torch.zeros((M, K), dtype=f16)
+    Wq = torch.zeros((N, K), dtype=i8t)
+    sw = torch.zeros((N,), dtype=f32)
+    Xq = torch.zeros((M, K), dtype=i8t)
+    sx = torch.zeros((M,), dtype=f32)
+    Xo = torch.zeros((M * ops.outlier_ld(K),), dtype=f16)
+    cols = torch.zeros((K,), dtype=i32)
+    n = torch.zeros((1,), dtype=i32)
+    ws = torch.zeros((ops.workspace_bytes(M, K),), dtype=torch.uint8)
+
+    def bad(fn, *a, **kw):
+        with pytest.raises(ValueError) as e:
+            fn(*a, **kw)
+        assert "GPU" not in str(e.value), e.value   # refused for its size, not its device
+
+    # layer call: out, bias, sw, Wq width, workspace
+    bad(ops.linear_int8_mixed, X, Wq, sw, out=torch.zeros((M * N - 1,), dtype=f16))
+    bad(ops.linear_int8_mixed, X, Wq, sw, bias=torch.zeros((N - 1,), dtype=f16))
+    bad(ops.linear_int8_mixed, X, Wq, torch.zeros((N + 1,), dtype=f32))
+    bad(ops.linear_int8_mixed, X, torch.zeros((N, K + 16), dtype=i8t), sw)
+    bad(ops.linear_int8_mixed, X, Wq, sw, workspace=ws[:-1])
+    bad(ops.linear_int8_mixed_fp16_weights, X, torch.zeros((N, K), dtype=f16),
+        torch.zeros((N, K - 16), dtype=i8t), sw)
+    bad(ops.linear_int8_mixed_fp16_weights, X, torch.zeros((N, K), dtype=f16), Wq,
+        torch.zeros((N - 1,), dtype=f32))
+    # step calls
+    bad(ops.int8_quantize_colwise_weight, torch.zeros((N, K), dtype=f16), Wq[:-1])
+    bad(ops.int8_quantize_colwise_weight, torch.zeros((N, K), dtype=f16), Wq, sw[:-1])
+    bad(ops.int8_quantize_rowwise, X, torch.zeros((K // 32 - 1,), dtype=i32))
+    bad(ops.int8_quantize_rowwise, X, None, Xq[:-1])
+    bad(ops.int8_quantize_rowwise, X, None, Xq, sx[:-1])
+    bad(ops.int8_mm_dequant, Xq, Wq, sx[:-1], sw)
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw[:-1])
+    bad(ops.int8_mm_dequant, Xq, torch.zeros((N, K + 16), dtype=i8t), sx, sw)
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, Xo[:-1], cols, n)
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, Xo, cols[:-1], n)
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, Xo, cols, torch.zeros((2,), dtype=i32))
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, Xo, cols, None)
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, bias=torch.zeros((N + 1,), dtype=f16))
+    bad(ops.int8_mm_dequant, Xq, Wq, sx, sw, out=torch.zeros((M, N - 1), dtype=f16))
+    bad(ops.gelu_f16, X, torch.zeros((M * K - 1,), dtype=f16))
+    with pytest.raises(TypeError):
+        ops.int8_mm_dequant(Xq, Wq, sx, sw, Xo, cols, n.to(torch.int64))
+    # the right sizes on the host: refused by the device check
+    for fn, a in [(ops.linear_int8_mixed, (X, Wq, sw)),
+                  (ops.int8_mm_dequant, (Xq, Wq, sx, sw, Xo, cols, n)),
+                  (ops.int8_quantize_rowwise, (X,))]:
+        with pytest.raises(ValueError, match="GPU"):
+            fn(*a)
 
 
 def _gpu_present():

@@ -26,6 +26,8 @@ pytestmark = pytest.mark.gpu
 # (M, K, N, planted outlier columns, bias, weight kept in fp16)
 CASES = {
     "m1_k4096_n4096": (1, 4096, 4096, 6, False, False),
+    "m4_k4096_n4096": (4, 4096, 4096, 6, False, False),
+    "m16_k4096_n4096": (16, 4096, 4096, 6, False, False),
     "m4_k16384": (4, 16384, 520, 10, True, False),
     "m5_k2064": (5, 2064, 300, 3, False, False),
     "m8_k8192_n40": (8, 8192, 257, 40, True, False),

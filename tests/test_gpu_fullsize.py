@@ -14,7 +14,7 @@ import torch
 
 from int8_quantized_matmul_absmax_amd import synth
 from oracle import llm_int8 as O
-from tests.gpu_helpers import Y_TOL, dev, host, note, sample_rows, y_err
+from tests.gpu_helpers import Y_TOL, dev, f16_ulp, host, note, sample_rows, y_err
 
 pytestmark = pytest.mark.gpu
 
@@ -109,15 +109,25 @@ def test_mlp_sweep_per_layer(gpu, n_in):
     assert np.array_equal(host(Wq1), Wq1_ref)
     ref1 = O.linear_int8_mixed(X, Wq1_ref, sw1_ref, 6.0)
     assert ref1["n"] >= n_in
-    Y1 = ops.linear_int8_mixed(dev(X), Wq1, sw1, None, 6.0)
+    K1, N1 = X.shape[1], Wq1.shape[0]
+    ws1 = torch.empty((ops.workspace_bytes(M, K1, N1),), dtype=torch.uint8, device="cuda")
+    Y1 = ops.linear_int8_mixed(dev(X), Wq1, sw1, None, 6.0, ws1)
     torch.cuda.synchronize()
     assert y_err(host(Y1), ref1["Y"]) <= Y_TOL
+    v1 = ops.workspace_views(ws1, M, K1)
+    assert np.array_equal(host(v1["Xq"]), ref1["Xq"])
+    rows1 = sample_rows(M, 64, 100 + n_in)
+    note("mlp n_in=%d layer 1 int32 accumulators on %d rows" % (n_in, rows1.size))
+    C1 = ops.int8_mm_dequant(v1["Xq"], Wq1, v1["sx"], sw1, want_y=False, want_int32=True)
+    C1_s = host(C1[torch.from_numpy(rows1).cuda()])
+    del C1
+    assert np.array_equal(C1_s, O.int32_accumulators(ref1["Xq"][rows1], Wq1_ref))
 
     # GELU between the layers: the oracle's chain (fp16 layer-1 output, exact
     # GELU, fp16) defines layer 2's input.
     G_ref = O.gelu_erf(ref1["Y"].astype(np.float16).astype(np.float64)).astype(np.float16)
     G_gpu = host(ops.gelu_f16(dev(ref1["Y"].astype(np.float16))))
-    ulp = np.spacing(np.abs(G_ref)).astype(np.float64)
+    ulp = f16_ulp(G_ref)
     assert np.all(np.abs(G_gpu.astype(np.float64) - G_ref.astype(np.float64)) <= ulp + 1e-12)
 
     note("mlp n_in=%d layer 2" % n_in)
@@ -136,6 +146,11 @@ def test_mlp_sweep_per_layer(gpu, n_in):
     rows = sample_rows(M, 128, n_in)
     ref2 = O.linear_int8_mixed(G_ref, Wq2_ref, sw2_ref, 6.0, rows=rows)
     assert np.array_equal(host(v["Xq"])[rows], ref2["Xq"])
+    note("mlp n_in=%d layer 2 int32 accumulators on %d rows" % (n_in, rows.size))
+    C2 = ops.int8_mm_dequant(v["Xq"], Wq2, v["sx"], sw2, want_y=False, want_int32=True)
+    C2_s = host(C2[torch.from_numpy(rows).cuda()])
+    del C2
+    assert np.array_equal(C2_s, O.int32_accumulators(ref2["Xq"], Wq2_ref))
     err2 = y_err(host(Y2)[rows], ref2["Y"])
     assert err2 <= Y_TOL, err2
     print("n_in=%d: layer-1 outliers %d, layer-2 outliers %d" % (n_in, ref1["n"], cols2.size))
