@@ -244,6 +244,34 @@ I8MM_API int linear_int8_mixed(const uint16_t* X, int64_t M, int64_t K,
                       void* workspace, size_t workspace_bytes, i8mm_stream_t stream);
 
 /*
+ * linear_int8_mixed_noalloc  (linear_int8_mixed without a workspace argument)
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same
+ * layer as linear_int8_mixed, with the same kernels and results; its
+ * workspace is the library's own scratch, a static device array of
+ * I8MM_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends. The
+ * call allocates nothing (no hipMalloc, no hipFree); on its first call on a
+ * device it looks up that device's scratch address.
+ *
+ *   X, Wq, sw, N, bias, threshold, Y  as in linear_int8_mixed.
+ *
+ * The sizes must satisfy linear_int8_mixed_workspace_bytes(M, K) <=
+ * I8MM_NOALLOC_SCRATCH_BYTES (for example M * K <= about 11 million:
+ * 2048 x 4096 fits), else EWORKSPACE and nothing is launched. Every call on
+ * one GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other host threads) race; calls ordered on one stream do not. The
+ * scratch keeps the last call's intermediates; no part of it needs to be
+ * zero on entry. Errors: EINVAL, EALIGN, EWORKSPACE, ERANGE, ENODEVICE,
+ * ELAUNCH.
+ */
+#define I8MM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+I8MM_API int linear_int8_mixed_noalloc(const uint16_t* X, int64_t M, int64_t K,
+                                       const int8_t* Wq, const float* sw, int64_t N,
+                                       const uint16_t* bias, float threshold, uint16_t* Y,
+                                       i8mm_stream_t stream);
+
+/*
  * linear_int8_mixed_fp16_weights  (the whole layer for a weight kept in fp16)
  *
  * [HF-blog] "Usage": with has_fp16_weights=True (the module's default, meant

@@ -14,6 +14,7 @@ I8MM_ENODEVICE = -4
 I8MM_ELAUNCH = -5
 I8MM_ERANGE = -6
 I8MM_MAX_K = 133144
+I8MM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/i8mm.h declares.
 EXPORTS = (
@@ -23,6 +24,7 @@ EXPORTS = (
     "outlier_detect_quantize",
     "int8_mm_dequant",
     "linear_int8_mixed",
+    "linear_int8_mixed_noalloc",
     "linear_int8_mixed_fp16_weights",
     "linear_int8_mixed_workspace_bytes",
     "linear_int8_mixed_workspace_bytes_many_outliers",
@@ -58,6 +60,7 @@ def _declare(lib):
         "int8_mm_dequant": ([vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
         "linear_int8_mixed": ([vp, i64, i64, vp, vp, i64, vp, f32, vp, vp, ctypes.c_size_t, vp],
                               i32),
+        "linear_int8_mixed_noalloc": ([vp, i64, i64, vp, vp, i64, vp, f32, vp, vp], i32),
         "linear_int8_mixed_fp16_weights": ([vp, i64, i64, vp, i64, vp, vp, i32, vp, f32, vp, vp,
                                             ctypes.c_size_t, vp], i32),
         "linear_int8_mixed_workspace_bytes": ([i64, i64], ctypes.c_size_t),

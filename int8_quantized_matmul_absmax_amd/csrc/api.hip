@@ -356,6 +356,62 @@ int outlier_detect_quantize(const uint16_t* X, int64_t M, int64_t K, float thres
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of linear_int8_mixed_noalloc, for callers that cannot allocate:
+// one copy per GPU the library runs on, held until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[I8MM_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (concurrent first calls look up the same address).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(I8MM_ENODEVICE, "%s: no HIP device: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(I8MM_ENODEVICE, "%s: device %d beyond the %d the library tracks", fn, dev,
+                kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(I8MM_ELAUNCH, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return I8MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int linear_int8_mixed_noalloc(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                              const float* sw, int64_t N, const uint16_t* bias, float threshold,
+                              uint16_t* Y, i8mm_stream_t stream) {
+  const char* fn = "linear_int8_mixed_noalloc";
+  I8MM_TRY(check_dims(fn, M, N, K));
+  int64_t off[7];
+  layout(M, K, off);
+  if (off[6] > (int64_t)I8MM_NOALLOC_SCRATCH_BYTES)
+    return fail(I8MM_EWORKSPACE,
+                "%s: M=%lld, K=%lld need %lld bytes of workspace, more than the %lld of the "
+                "library's scratch; use linear_int8_mixed with a workspace",
+                fn, (long long)M, (long long)K, (long long)off[6],
+                (long long)I8MM_NOALLOC_SCRATCH_BYTES);
+  I8MM_TRY(check_device());
+  void* ws = nullptr;
+  I8MM_TRY(scratch_address(fn, &ws));
+  return run_layer(fn, X, M, K, Wq, sw, N, bias, threshold, Y, ws,
+                   (size_t)I8MM_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream, nullptr, false);
+}
+
 int i8mm_gelu_f16(const uint16_t* X, int64_t count, uint16_t* Y, i8mm_stream_t stream) {
   const char* fn = "i8mm_gelu_f16";
   if (count < 0) return fail(I8MM_EINVAL, "%s: negative count", fn);
