@@ -505,18 +505,23 @@ def _profile_kernels():
     done = []
 
     def section(name):
+        """Start of a section's measured work (its end is the next end())."""
         mark()
         done.append(name)
         log("profile section " + name)
 
+    def end():
+        mark()
+
     # copy probe: a plain copy of known size (the counters' calibration)
     src = torch.empty((COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
-    dst = torch.empty((COPY_PROBE_BYTES,), dtype=torch.int8, device="cuda")
+    dst = torch.empty_like(src)
     src.fill_(3)
     torch.cuda.synchronize()
     section("copy_probe")
     for _ in range(3):
         dst.copy_(src)
+    end()
     del src, dst
 
     d = synth.ffn_175b()
@@ -528,12 +533,14 @@ def _profile_kernels():
     section("ffn175b_weight_quant")
     for _ in range(2):
         ops.int8_quantize_colwise_weight(W, Wq, sw)
+    end()
     del W
     ws = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
     Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     section("ffn175b_layer")
     for _ in range(3):
         ops.linear_int8_mixed(X, Wq, sw, None, 6.0, ws, Y)
+    end()
     del X, Wq, sw, ws, Y, d
 
     d = synth.opt_ffn_up()
@@ -547,6 +554,7 @@ def _profile_kernels():
     for i in range(4):
         Xs, Wqs, wss, Ys = sets[i]
         ops.linear_int8_mixed(Xs, Wqs, sw, None, 6.0, wss, Ys)
+    end()
     del sets, Wq0, d
 
     for m in (1, 4, 16):
@@ -561,6 +569,7 @@ def _profile_kernels():
         section("decode_m%d" % m)
         for i in range(3):
             ops.linear_int8_mixed(X, copies[7 * i + 3], sw, None, 6.0, ws, Y)
+        end()
         del copies, X, ws, Y, d
 
     d = synth.mlp_sweep(32)
@@ -575,7 +584,7 @@ def _profile_kernels():
     section("mlp_n32_layer2")
     for _ in range(2):
         ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2)
-    mark()
+    end()
     torch.cuda.synchronize()
     print(json.dumps({"profile_sections": done}), flush=True)
 
@@ -618,15 +627,18 @@ def _family(name):
     return s.split("<")[0] if s.startswith("k_") else ("copy" if "copy" in name.lower() else s)
 
 
+def _is_marker(name):
+    return "fill" in name.lower() and "double" in name.lower()
+
+
 def _split_sections(disp, sections):
-    """Dispatch list -> {section: [dispatches]}, cut at the marker fills."""
-    marks = [i for i, d in enumerate(disp) if "fill" in d[1].lower() and "double" in d[1].lower()]
-    out = {}
-    for j, name in enumerate(sections):
-        a = marks[j] + 1
-        b = marks[j + 1] if j + 1 < len(marks) else len(disp)
-        out[name] = disp[a:b]
-    return out
+    """Dispatch list -> {section: [dispatches]}: section j is what lies between
+    the marker fills 2j and 2j+1 (its start and end); the set-up work between
+    one section's end and the next one's start belongs to none."""
+    marks = [i for i, d in enumerate(disp) if _is_marker(d[1])]
+    if len(marks) != 2 * len(sections):
+        raise SystemExit("expected %d marker dispatches, found %d" % (2 * len(sections), len(marks)))
+    return {name: disp[marks[2 * j] + 1:marks[2 * j + 1]] for j, name in enumerate(sections)}
 
 
 SECTION_WORK = {
@@ -647,7 +659,9 @@ def _write_counters(pmc_dir):
     of one XCD / kernel duration."""
     sections = json.load(open(os.path.join(pmc_dir, "manifest.json")))["profile_sections"]
     runs = {}
-    for run in ("trace", "mfma", "dram", "fetch", "write"):
+    for run in ("trace", "mfma", "dram", "fetch", "write", "lds"):
+        if run == "lds" and not os.path.isdir(os.path.join(pmc_dir, run)):
+            continue
         sub = os.path.join(pmc_dir, run)
         f = [x for x in os.listdir(sub) if x.endswith(("counter_collection.csv", "kernel_trace.csv"))]
         runs[run] = _split_sections(_dispatches(os.path.join(sub, f[0])), sections)
@@ -656,8 +670,14 @@ def _write_counters(pmc_dir):
         vals = [d[2].get(key) for d in runs[run][sec] if _family(d[1]) == fam and key in d[2]]
         return sum(vals) / len(vals) if vals else None
 
-    def durs(sec, fam):
-        v = [d[3] for d in runs["trace"][sec] if _family(d[1]) == fam and d[3]]
+    def durs(sec, fam, run="trace"):
+        v = [d[3] for d in runs[run][sec] if _family(d[1]) == fam and d[3]]
+        return sum(v) / len(v) if v else None
+
+    def per_dispatch(run, sec, fam, f):
+        """Mean over the family's dispatches of f(counters, duration ns)."""
+        v = [f(d[2], d[3]) for d in runs[run][sec] if _family(d[1]) == fam and d[3]]
+        v = [x for x in v if x is not None]
         return sum(v) / len(v) if v else None
 
     cp = "copy_probe"
@@ -682,6 +702,10 @@ def _write_counters(pmc_dir):
                "python3 bench.py --profile-kernels" % pmc_dir,
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s/write -o run -- "
                "python3 bench.py --profile-kernels" % pmc_dir,
+               "rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS_LOAD_BANDWIDTH "
+               "SQ_LDS_DATA_FIFO_FULL SQ_WAIT_INST_LDS SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
+               "--output-format csv -d %s/lds -o run -- python3 bench.py --profile-kernels"
+               % pmc_dir,
                "python3 bench.py --profile-kernels > %s/manifest.json" % pmc_dir,
                "python3 bench.py --write-counters %s" % pmc_dir],
            "calibration": {
@@ -722,14 +746,43 @@ def _write_counters(pmc_dir):
             if act:
                 act1 = act / 8.0     # GRBM_GUI_ACTIVE summed over the 8 XCDs
                 e["active_cycles_per_xcd"] = round(act1)
-                if t_ns:
-                    e["effective_clock_ghz"] = round(act1 / t_ns, 3)
+                # clock: active cycles of one XCD over the same dispatch's own
+                # duration in the counter run
+                clk = per_dispatch("mfma", sec, fam,
+                                   lambda c, t: c["GRBM_GUI_ACTIVE"] / 8.0 / t
+                                   if "GRBM_GUI_ACTIVE" in c else None)
+                if clk is not None:
+                    e["effective_clock_ghz"] = round(clk, 3)
+                    e["duration_us_counter_run"] = round(durs(sec, fam, "mfma") / 1e3, 3)
                 if busy is not None:
                     e["mfma_busy_frac"] = round(busy / (act1 * 1024.0), 4)
                 if mi8 is not None:
                     e["mfma_i8_ops"] = round(mi8 * 512)
                 if mf16 is not None:
                     e["mfma_f16_flops"] = round(mf16 * 512)
+            if "lds" in runs:
+                la = mean("lds", sec, fam, "GRBM_GUI_ACTIVE")
+                if la:
+                    la1 = la / 8.0
+                    idx = mean("lds", sec, fam, "SQ_LDS_IDX_ACTIVE")
+                    bc = mean("lds", sec, fam, "SQ_LDS_BANK_CONFLICT")
+                    bw = mean("lds", sec, fam, "SQ_INSTS_LDS_LOAD_BANDWIDTH")
+                    ff = mean("lds", sec, fam, "SQ_LDS_DATA_FIFO_FULL")
+                    wl = mean("lds", sec, fam, "SQ_WAIT_INST_LDS")
+                    bu = mean("lds", sec, fam, "SQ_BUSY_CU_CYCLES")
+                    if idx is not None:
+                        e["lds_active_frac"] = round(idx / (la1 * 256.0), 4)
+                    if bc is not None and idx:
+                        e["lds_bank_conflict_of_active"] = round(bc / idx, 4)
+                    if bw is not None:
+                        e["lds_load_bytes"] = round(bw * 64)
+                        e["lds_load_bytes_per_cu_cycle"] = round(bw * 64 / (la1 * 256.0), 2)
+                    if ff is not None:
+                        e["lds_data_fifo_full_frac"] = round(ff / (la1 * 256.0), 4)
+                    if wl is not None:
+                        e["wait_inst_lds_wave_cycles"] = round(wl * 4)
+                    if bu is not None:
+                        e["cu_busy_frac"] = round(bu * 4 / (la1 * 256.0), 4)
             ks[fam] = e
         rec["sections"][sec] = {"kernels": ks}
     with open(COUNTERS_FILE, "w") as f:
@@ -741,15 +794,17 @@ def _write_counters(pmc_dir):
     out += ["", "Calibration on the copy probe (%d bytes read and written): %s" % (
         COPY_PROBE_BYTES, json.dumps(rec["calibration"])), "", rec["notes"], "",
         "| section | kernel | avg us (trace) | DRAM read MB | DRAM write MB | fetch+write MB "
-        "| clock GHz | MFMA busy | MFMA i8 ops | MFMA f16 flops |", "|---|---|---|---|---|---|---|---|---|---|"]
+        "| clock GHz | MFMA busy | MFMA i8 ops | MFMA f16 flops | LDS active | LDS B/CU-clk |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for sec, v in rec["sections"].items():
         for fam, e in v["kernels"].items():
             g = lambda k, s=1e6: ("%.2f" % (e[k] / s)) if e.get(k) is not None else ""
-            out.append("| %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            out.append("| %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
                 sec, fam, e.get("avg_duration_us", ""), g("dram_read_bytes"),
                 g("dram_write_bytes"), g("fetch_write_bytes"), e.get("effective_clock_ghz", ""),
                 e.get("mfma_busy_frac", ""), "%.4g" % e["mfma_i8_ops"] if e.get("mfma_i8_ops") else "",
-                "%.4g" % e["mfma_f16_flops"] if e.get("mfma_f16_flops") else ""))
+                "%.4g" % e["mfma_f16_flops"] if e.get("mfma_f16_flops") else "",
+                e.get("lds_active_frac", ""), e.get("lds_load_bytes_per_cu_cycle", "")))
     out += ["", "Kernel code SHA-256 (comments and whitespace ignored): " + rec["kernel_code_sha256"]]
     with open(COUNTERS_MD, "w") as f:
         f.write("\n".join(out) + "\n")

@@ -89,7 +89,7 @@ def test_counter_summary_from_rocprof_csvs(tmp_path, monkeypatch):
     gemm = ("void i8mm::(anonymous namespace)::k_gemm_i8<i8mm::(anonymous namespace)::"
             "GemmCfg<256, 256, 64, 5, 4>, 0>(signed char const*)")
     rows_k = "void i8mm::(anonymous namespace)::k_rows<24, 2>(unsigned short const*)"
-    seq = [mark, copy, copy, mark, rows_k, gemm, gemm, mark]
+    seq = [mark, copy, copy, mark, rows_k, mark, rows_k, gemm, gemm, mark]
     sections = ["copy_probe", "layer"]
     (tmp_path / "pmc").mkdir()
     (tmp_path / "pmc" / "manifest.json").write_text(json.dumps({"profile_sections": sections}))
@@ -107,9 +107,10 @@ def test_counter_summary_from_rocprof_csvs(tmp_path, monkeypatch):
         rows = []
         for i, k in enumerate(seq):
             for c, f in values.items():
-                rows.append([i + 1, k, c, f(k)])
+                rows.append([i + 1, k, c, f(k), trace[i][2], trace[i][3]])
         _write_csv(tmp_path / "pmc" / run / "run_counter_collection.csv",
-                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"], rows)
 
     half = bench.COPY_PROBE_BYTES
     counters("dram", {"TCC_EA0_RDREQ_DRAM_sum": lambda k: half / 64 if k == copy else 1000.0,
@@ -136,5 +137,7 @@ def test_counter_summary_from_rocprof_csvs(tmp_path, monkeypatch):
     assert g["mfma_busy_frac"] == 0.5
     assert g["mfma_i8_ops"] == 51200
     assert set(rec["sections"]["layer"]["kernels"]) == {"k_rows", "k_gemm_i8"}
+    # the set-up dispatch between the sections (a k_rows) belongs to neither
+    assert rec["sections"]["layer"]["kernels"]["k_rows"]["dram_read_bytes"] == 64000
     assert set(rec["sections"]["copy_probe"]["kernels"]) == {"copy"}
     assert "k_gemm_i8" in open(tmp_path / "out.md").read()
