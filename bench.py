@@ -345,7 +345,9 @@ def _measure_mlp(ops, prewarm_ms, stream):
     """The two-layer MLP block (1024 x 4096 -> 16384 -> GELU -> 4096) per
     planted outlier density: layer times, layer 2's emergent outlier count,
     and each layer's GEMM roofline fraction (int8 and fp16 work at their own
-    peaks). Same buffers every call (the 67 MB weights may sit in the MALL)."""
+    peaks). Layer 2 is timed with the default workspace (room for 512 outlier
+    weight columns) and with one that has room for every count. Same buffers
+    every call (the 67 MB weights may sit in the MALL)."""
     import torch
     from int8_quantized_matmul_absmax_amd import synth
     rows = []
@@ -359,6 +361,8 @@ def _measure_mlp(ops, prewarm_ms, stream):
         del d
         ws1 = torch.empty((ops.workspace_bytes(M, H, F),), dtype=torch.uint8, device="cuda")
         ws2 = torch.empty((ops.workspace_bytes(M, F, H),), dtype=torch.uint8, device="cuda")
+        ws2_all = torch.empty((ops.workspace_bytes_all_outliers(M, F, H),), dtype=torch.uint8,
+                              device="cuda")
         Y1 = torch.empty((M, F), dtype=torch.float16, device="cuda")
         G = torch.empty_like(Y1)
         Y2 = torch.empty((M, H), dtype=torch.float16, device="cuda")
@@ -374,14 +378,19 @@ def _measure_mlp(ops, prewarm_ms, stream):
         tg, _ = _timed(lambda i: ops.gelu_f16(Y1, G), 20, 2, 0, stream)
         t2, _ = _timed(lambda i: ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2), 20, 2,
                        min(prewarm_ms, 150), stream)
+        t2a, _ = _timed(lambda i: ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2_all, Y2), 20,
+                        2, min(prewarm_ms, 150), stream)
         _, _, f1, _ = _mfma_roofline(M, F, H, n1, t1)
         _, _, f2, _ = _mfma_roofline(M, H, F, n2, t2)
+        _, _, f2a, _ = _mfma_roofline(M, H, F, n2, t2a)
         rows.append({"n_in": n_in, "n_layer1": n1, "n_layer2": n2,
                      "us_layer1": round(t1 * 1e3, 2), "us_gelu": round(tg * 1e3, 2),
                      "us_layer2": round(t2 * 1e3, 2),
+                     "us_layer2_room_all": round(t2a * 1e3, 2),
                      "layer1_mfma_frac": round(f1, 4), "layer2_mfma_frac": round(f2, 4),
+                     "layer2_room_all_mfma_frac": round(f2a, 4),
                      "layer2_fp16_flops": 2 * M * H * n2})
-        del X, Wq1, Wq2, ws1, ws2, Y1, G, Y2
+        del X, Wq1, Wq2, ws1, ws2, ws2_all, Y1, G, Y2
     base = rows[0]
     for r in rows:
         r["overhead_us_vs_n0"] = round(r["us_layer1"] + r["us_layer2"]

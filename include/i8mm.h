@@ -229,10 +229,11 @@ I8MM_API int outlier_detect_quantize(const uint16_t* X, int64_t M, int64_t K, fl
  *   workspace  device buffer of at least linear_int8_mixed_workspace_bytes(M,K)
  *              bytes, 256-byte aligned; it receives the intermediates (outlier
  *              bitmap, cols, n, sx, Xq, Xo) at the offsets that
- *              i8mm_workspace_layout reports. Given at least
- *              linear_int8_mixed_workspace_bytes_many_outliers(M, K, N) bytes,
- *              the recovered outlier weight columns go after them (see that
- *              call) and many outlier columns take the fast path.
+ *              i8mm_workspace_layout reports. Bytes beyond
+ *              linear_int8_mixed_workspace_bytes(M, K) are a region for the
+ *              recovered outlier weight columns, with room for
+ *              floor(extra / (2 N) / 32) * 32 columns (see
+ *              linear_int8_mixed_workspace_bytes_many_outliers).
  *
  * All kernels run in order on `stream` with no host synchronization; the
  * outlier count stays on the device. Errors: EINVAL, EALIGN, EWORKSPACE,
@@ -312,17 +313,31 @@ I8MM_API int linear_int8_mixed_fp16_weights(const uint16_t* X, int64_t M, int64_
  * (0 if the sizes are invalid). Host-only, pure. */
 I8MM_API size_t linear_int8_mixed_workspace_bytes(int64_t M, int64_t K);
 
-/* Bytes of workspace with which linear_int8_mixed also takes its fast path
- * for many outlier columns (0 if the sizes are invalid). Host-only, pure.
- * It is the size above plus a region, starting at
- * linear_int8_mixed_workspace_bytes(M, K), for the recovered fp16 weight
- * columns of the outlier columns ([HF-blog] "Usage": CB * SCB / 127 per
- * output row), Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)),
- * N rows of I8MM_OUTLIER_LD(n) halfs. With more than 16 outlier columns (and
- * more than 64 tokens) the layer fills that region and runs the outlier
- * product as a second main loop of its GEMM over the outlier columns; given
- * only the smaller workspace it computes the same result with the outlier
- * product in the GEMM's epilogue, which is slow for many outlier columns. */
+/* Outlier columns the region of
+ * linear_int8_mixed_workspace_bytes_many_outliers has room for. */
+#define I8MM_OUTLIER_REGION_COLS 512
+
+/* Bytes of workspace with a region for the recovered fp16 weight columns of
+ * up to I8MM_OUTLIER_REGION_COLS outlier columns (0 if the sizes are
+ * invalid). Host-only, pure. It is linear_int8_mixed_workspace_bytes(M, K)
+ * plus N rows of I8MM_OUTLIER_LD(min(K, I8MM_OUTLIER_REGION_COLS)) halfs.
+ *
+ * The region starts at linear_int8_mixed_workspace_bytes(M, K) and holds the
+ * recovered weights ([HF-blog] "Usage": CB * SCB / 127 per output row),
+ * Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)), N rows of
+ * I8MM_OUTLIER_LD(n) halfs. Any workspace larger than the minimal one has
+ * such a region: its room is floor(extra bytes / (2 N) / 32) * 32 columns
+ * (at most I8MM_OUTLIER_LD(K)), so a caller with memory to spare may pass
+ * more than this size (N * I8MM_OUTLIER_LD(K) * 2 extra bytes give room for
+ * every count). With more than 16 outlier columns, room for them and more
+ * than 64 tokens, the layer fills the region and runs the outlier product
+ * as a second main loop of its GEMM over those columns. Otherwise (more than
+ * 16 columns) the GEMM runs the outlier product as a second loop over all K
+ * columns, converting the int8 weight tile to fp16 itself (the recovered
+ * weights' factor sw[j] / 127 applied to the sum): every outlier count runs
+ * without a region, and the region speeds up the counts it has room for.
+ * The two loops sum in different orders, so Y may differ in the last bits
+ * between them (both within the tolerance of the method). */
 I8MM_API size_t linear_int8_mixed_workspace_bytes_many_outliers(int64_t M, int64_t K, int64_t N);
 
 /* Byte offsets inside the workspace, host-only and pure. Writes, in order:

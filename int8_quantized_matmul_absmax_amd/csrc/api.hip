@@ -2,6 +2,7 @@
 // launch sequence of each entry point. Declarations and the contract of each
 // call are in include/i8mm.h.
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -101,10 +102,11 @@ bool layout(int64_t M, int64_t K, int64_t* off, int64_t* part = nullptr) {
   return true;
 }
 
-// Bytes of the optional region after the minimal workspace: the recovered
-// fp16 outlier weight columns, [N, I8MM_OUTLIER_LD(K)] at most.
+// Bytes of the region of linear_int8_mixed_workspace_bytes_many_outliers
+// after the minimal workspace: the recovered fp16 outlier weight columns
+// for up to I8MM_OUTLIER_REGION_COLS outlier columns.
 int64_t wo_region_bytes(int64_t N, int64_t K) {
-  return round_up(N * I8MM_OUTLIER_LD(K) * 2, kAlign);
+  return round_up(N * I8MM_OUTLIER_LD(std::min<int64_t>(K, I8MM_OUTLIER_REGION_COLS)) * 2, kAlign);
 }
 
 }  // namespace
@@ -221,8 +223,8 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
   I8MM_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr,
-                        nullptr, s),
+      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr, 0,
+                        nullptr, nullptr, nullptr, s),
       fn));
   return ok();
 }
@@ -303,18 +305,27 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
     return ok();
   }
   I8MM_TRY(x_side(fn, X, M, K, tau16, ws, off, off_part, s));
-  // With room for it, the fp16 outlier weight columns are materialized for
-  // the tiled GEMM (the kernels do nothing for 16 or fewer columns).
+  // The workspace beyond the minimal layout holds the recovered fp16 outlier
+  // weight columns for the tiled GEMM, N rows of LD(n) halfs, for n up to the
+  // columns it has room for (the kernels do nothing for 16 or fewer columns,
+  // or for more than that room; the GEMM's dense loop takes those).
   uint16_t* Wo = nullptr;
-  if (!i8mm::gemv_applies(M) && (int64_t)workspace_bytes >= off[6] + wo_region_bytes(N, K)) {
-    Wo = reinterpret_cast<uint16_t*>(ws + off[6]);
-    if (Wf)
-      I8MM_TRY(launched(i8mm::launch_gather_w_cols(Wf, N, K, cols, n_o, Wo, s), fn));
-    else
-      I8MM_TRY(launched(i8mm::launch_recover_outlier_w(Wq, sw, N, K, cols, n_o, Wo, s), fn));
+  int wo_cols = 0;
+  if (!i8mm::gemv_applies(M)) {
+    const int64_t room = ((int64_t)workspace_bytes - off[6]) / (2 * N) / 32 * 32;
+    if (room >= 32) {
+      wo_cols = (int)std::min<int64_t>(room, I8MM_OUTLIER_LD(K));
+      Wo = reinterpret_cast<uint16_t*>(ws + off[6]);
+      if (Wf)
+        I8MM_TRY(launched(i8mm::launch_gather_w_cols(Wf, N, K, cols, n_o, wo_cols, Wo, s), fn));
+      else
+        I8MM_TRY(launched(
+            i8mm::launch_recover_outlier_w(Wq, sw, N, K, cols, n_o, wo_cols, Wo, s), fn));
+    }
   }
-  I8MM_TRY(launched(
-      i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr, Wo, Wf, s), fn));
+  I8MM_TRY(launched(i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr,
+                                      Wo, wo_cols, Wf, X, bitmap, s),
+                    fn));
   return ok();
 }
 

@@ -99,6 +99,18 @@ __device__ __forceinline__ uint2 codes8_rne(const uint4& t, float s) {
                     __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
 }
 
+// Buffer descriptor over [base, base + bytes): loads past `bytes` return 0,
+// stores past it are dropped. The fields go through readfirstlane so the
+// descriptor lives in SGPRs (callers pass wave-uniform values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
 // Workgroup barrier for data exchanged through LDS only: this wave's LDS
 // operations complete (lgkmcnt(0), gfx9 encoding), then s_barrier, with no
 // fence on global memory, so nothing in flight there is waited for. The

@@ -72,6 +72,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "i8mm.h"
 #include "launchers.h"
 
 namespace i8mm {
@@ -168,21 +169,24 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
 
 // Kernel modes, separate instantiations so that each carries only its code
 // (register pressure):
-//   kPlain   fp16 output; outlier product in the epilogue. Given Wo, it
-//            returns at once when there are more than 16 outlier columns
-//            (kOutlierSeg does those).
+//   kPlain   fp16 output; outlier product in the epilogue. Returns at once
+//            when one of the two segment modes below takes the layer.
 //   kInt32   kPlain that also writes the raw int32 accumulators (parity mode).
-//   kOutlierSeg  only for more than 16 outlier columns with Wo given
-//            (returns at once otherwise): the outlier product as a second
-//            main-loop segment.
-enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2 };
+//   kOutlierSeg  only for more than 16 outlier columns with Wo given and
+//            room for them in it, wo_cols (returns at once otherwise): the
+//            outlier product as a second main-loop segment.
+//   kDenseSeg  more than 16 outlier columns, X given, and Wo not given or
+//            without room for them (returns at once otherwise): the
+//            outlier product as a dense second segment over all K columns.
+enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2, kDenseSeg = 3 };
 template <class Cfg, int MODE>
 __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
     const float* __restrict__ sw, int M, int N, int K, const uint16_t* __restrict__ Xo,
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C,
-    const uint16_t* __restrict__ Wo, const uint16_t* __restrict__ Wf) {
+    const uint16_t* __restrict__ Wo, int wo_cols, const uint16_t* __restrict__ Wf,
+    const uint16_t* __restrict__ Xd, const uint32_t* __restrict__ bmp) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN, KS = Cfg::KS;
   constexpr int LOADS = Cfg::LOADS, RPL = Cfg::ROWS_PER_LOAD;
@@ -212,14 +216,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // chunks (more than 16 outlier columns) are read in the epilogue.
   const int n_o = (Xo && cols && n_out && Y) ? *n_out : 0;
   const int64_t ldo = ((int64_t)n_o + 31) / 32 * 32;
-  // More than 16 outlier columns with the recovered weights materialized (Wo
-  // [N, ldo] fp16): the outlier product runs as a second main-loop segment
-  // over the outlier columns (fp16 MFMA on Wo and Xo through the same stage
-  // pipeline) instead of in the epilogue.
   constexpr bool WITH_C = MODE == kInt32;
-  const bool many = Wo != nullptr && n_o > 16;
-  if (MODE == kOutlierSeg ? !many : many) return;   // the other mode's case
-  constexpr bool seg2 = MODE == kOutlierSeg;
+  // With more than 16 outlier columns the outlier product runs as a second
+  // segment: over the materialized recovered weights Wo ([N, ldo] fp16) and
+  // Xo when the columns fit Wo's region (compact), else over all K columns
+  // with the weight tile converted in the kernel and X itself (dense, X
+  // given). Either runs fp16 MFMA through the same stage pipeline.
+  const bool compact = n_o > 16 && Wo != nullptr && n_o <= wo_cols;
+  const bool dense_case = n_o > 16 && !compact && Xd != nullptr && bmp != nullptr;
+  // each mode returns at once when the case is another mode's
+  if (MODE == kOutlierSeg && !compact) return;
+  if (MODE == kDenseSeg && !dense_case) return;
+  if ((MODE == kPlain || MODE == kInt32) && (compact || dense_case)) return;
+  constexpr bool seg2 = MODE == kOutlierSeg || MODE == kDenseSeg;
+  constexpr bool dense = MODE == kDenseSeg;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
   // Values held in registers from the prologue to the end of the main loop
@@ -498,6 +508,149 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     if (k < steps) step(k, 1, f16);
     wait_vmcnt<0>();
   };
+  // Dense outlier segment: the outlier product over all K columns, 32 columns
+  // per stage, three stage buffers, one barrier per stage, in the main loop's
+  // LDS layout (weight rows, then token rows, 64 bytes each, same swizzle),
+  // so the fragment reads and fp16 MFMAs are those of the compact segment.
+  // The weight tile comes through registers: thread t converts 16 columns of
+  // weight row t / 2 exactly to fp16 (the int8 codes, or the fp16 weight Wf
+  // itself) with the normal columns zeroed (bitmap word of the stage), and
+  // writes them to LDS. The token rows are X itself, by DMA: X is finite on
+  // the normal columns (a column holding inf or NaN is an outlier column),
+  // so the zeroed weights remove them exactly. A stage whose bitmap word is 0
+  // issues no MFMA.
+  auto dense_segment = [&]() __attribute__((always_inline)) {
+    constexpr int DNB = 3;
+    constexpr int DLB = BM / 16 / Cfg::WAVES;   // token-row DMA loads per wave and stage
+    static_assert(Cfg::THREADS == 2 * BN, "two threads per weight row");
+    static_assert(DLB * 16 * Cfg::WAVES == BM && DLB == 2, "token rows per wave");
+    static_assert(DNB * Cfg::STAGE_BYTES + 4 * ((I8MM_MAX_K + 31) / 32) <= Cfg::LDS_BYTES,
+                  "stages and the bitmap copy fit");
+    const int S = (K + 31) / 32;
+    uint32_t* s_dbm = reinterpret_cast<uint32_t*>(stages + DNB * Cfg::STAGE_BYTES);
+    for (int w = tid; w < S; w += Cfg::THREADS) s_dbm[w] = bmp[w];
+    // weight side: row ra, columns 16 * hf .. of each stage
+    const int ra = tid >> 1, hf = tid & 1;
+    const int rows_a = (int)min<int64_t>(BN, N - n0);
+    const bool wide = Wf != nullptr;   // fp16 weight: 32 bytes a thread
+    const __amdgpu_buffer_rsrc_t rsa = wide
+        ? make_rsrc(Wf + n0 * K, (uint32_t)rows_a * (uint32_t)K * 2u)
+        : make_rsrc(Wq + n0 * K, (uint32_t)rows_a * (uint32_t)K);
+    const int key_a = swz_key(ra);
+    uint4 areg[2][2];
+    auto load_a = [&](int st, int set) {
+      const int col = st * 32 + 16 * hf;
+      const bool ok = col < K;
+      if (wide) {
+        const int off = ok ? (ra * K + col) * 2 : 0x7fffffe0;
+        areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+        areg[set][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off + 16, 0, 0));
+      } else {
+        const int off = ok ? ra * K + col : 0x7ffffff0;
+        areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+      }
+    };
+    // token side: wave w fills token rows w * 32 + 16 p + lane / 4
+    const int rows_b = (int)min<int64_t>(BM, M - m0);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(Xd + m0 * K, (uint32_t)rows_b * (uint32_t)K * 2u);
+    int vb[DLB];
+    bool okb[DLB];
+#pragma unroll
+    for (int p = 0; p < DLB; ++p) {
+      const int rb = wave * (16 * DLB) + 16 * p + (lane >> 2);
+      const int c = (lane & 3) ^ swz_key(BN + rb);
+      okb[p] = rb < rows_b;
+      vb[p] = okb[p] ? rb * K * 2 + c * 16 : 0;
+    }
+    const int cb = ((lane & 3) ^ swz_key(BN + wave * (16 * DLB) + (lane >> 2))) * 16;
+    auto load_b = [&](int st) {
+      int8_t* sbase = stages + (st % DNB) * Cfg::STAGE_BYTES + (BN + wave * 16 * DLB) * BK;
+      const int soff = __builtin_amdgcn_readfirstlane(st * 64);
+#pragma unroll
+      for (int p = 0; p < DLB; ++p) {
+        const bool ok = okb[p] && st * 64 + cb < 2 * K;
+        const int vo = ok ? vb[p] : 0x7ffffff0 - soff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + p * 16 * BK), 16, vo,
+                                                 soff, 0, 0);
+      }
+    };
+    // 4 int8 codes -> 4 fp16 (exact): bytes b + 128 under the exponent of
+    // 1024 give 1024 + b + 128, minus 1152
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    auto cvt4 = [](uint32_t d) -> uint2 {
+      const uint32_t u = d ^ 0x80808080u;
+      const h2 k = h2{(_Float16)1152.0f, (_Float16)1152.0f};
+      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - k;
+      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - k;
+      return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    };
+    auto write_a = [&](int st, int set, uint32_t word) {
+      const uint32_t bits = (word >> (16 * hf)) & 0xffffu;   // outlier columns of the 16
+      uint32_t h[8];
+      if (wide) {
+        const uint32_t w8[8] = {areg[set][0].x, areg[set][0].y, areg[set][0].z, areg[set][0].w,
+                                areg[set][1].x, areg[set][1].y, areg[set][1].z, areg[set][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b2 = (bits >> (2 * i)) & 3u;
+          h[i] = w8[i] & (((b2 & 1u) | ((b2 & 2u) << 15)) * 0xffffu);
+        }
+      } else {
+        const uint32_t w4[4] = {areg[set][0].x, areg[set][0].y, areg[set][0].z, areg[set][0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t b4 = (bits >> (4 * i)) & 15u;
+          const uint32_t keep = ((b4 * 0x00204081u) & 0x01010101u) * 0xffu;
+          const uint2 c = cvt4(w4[i] & keep);
+          h[2 * i] = c.x;
+          h[2 * i + 1] = c.y;
+        }
+      }
+      int8_t* row = stages + (st % DNB) * Cfg::STAGE_BYTES + ra * BK;
+      *reinterpret_cast<uint4*>(row + (((2 * hf) ^ key_a) << 4)) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(row + (((2 * hf + 1) ^ key_a) << 4)) = make_uint4(h[4], h[5], h[6], h[7]);
+    };
+    const std::integral_constant<bool, true> f16{};
+    // step st: its weight registers and token DMA have landed (only stage
+    // st + 1's loads may be in flight), weights to LDS, barrier (stage st
+    // visible; every wave is done with stage st - 1, whose buffer the loads of
+    // stage st + 2 then take), the loads of stage st + 2, the MFMAs of st.
+    auto dstep = [&](int st, int set) __attribute__((always_inline)) {
+      const bool more = st + 1 < S;
+      if (wide) {
+        if (more) wait_vmcnt<2 + DLB>(); else wait_vmcnt<0>();
+      } else {
+        if (more) wait_vmcnt<1 + DLB>(); else wait_vmcnt<0>();
+      }
+      const uint32_t word = s_dbm[st];
+      write_a(st, set, word);
+      lds_barrier();
+      if (st + 2 < S) {
+        load_a(st + 2, set);
+        load_b(st + 2);
+      }
+      if (word) {
+        const int8_t* base = stages + (st % DNB) * Cfg::STAGE_BYTES;
+#pragma unroll
+        for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, 0);
+#pragma unroll
+        for (int m = 0; m < Cfg::NMFMA; ++m) mfma_one(m, 0, f16);
+      }
+    };
+    lds_barrier();   // the bitmap copy is in LDS (read by every step)
+    load_a(0, 0);
+    load_b(0);
+    if (S > 1) {
+      load_a(1, 1);
+      load_b(1);
+    }
+    for (int st = 0; st < S; st += 2) {
+      dstep(st, 0);
+      if (st + 1 < S) dstep(st + 1, 1);
+    }
+    wait_vmcnt<0>();
+  };
+
   // Prologue: the row / column factors are read into registers, then the
   // first four stages are issued with the chunk-0 outlier gathers between
   // stages 0-1 and 2-3; factors and gathers go to LDS after the main loop.
@@ -533,8 +686,13 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   if (seg2) {
     lds_barrier();   // the factors are in LDS
     // Dequantize in place, C * (sx/127) * (sw/127) in fp32 (the same
-    // expression as the epilogue's), then the outlier segment adds
-    // sum_t Xo[i, t] * Wo[j, t] onto it.
+    // expression as the epilogue's), then the compact segment adds
+    // sum_t Xo[i, t] * Wo[j, t] onto it. The dense segment over the int8
+    // weight adds sum_{k in O} X[i, k] * q[j, k] onto C * (sx/127) and the
+    // epilogue multiplies by sw/127: the recovered weight q * sw / 127 per
+    // output row ([HF-blog] "Usage"), its factor taken out of the sum. Over
+    // the fp16 weight (Wf) it adds sum_{k in O} X[i, k] * Wf[j, k] onto the
+    // whole dequantized value, as the compact segment does.
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
       float fw[16];
@@ -543,19 +701,29 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       for (int b = 0; b < TM; ++b) {
         const float ax = s_ax[wm * WM + b * 32 + l32];
         v16f32 y;
+        if (dense && Wf == nullptr) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax * fw[r];
+          for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax * fw[r];
+        }
         acc[a][b] = __builtin_bit_cast(v16i32, y);
       }
     }
-    const uint16_t* seg_base = loads_w ? Wo + n0 * ldo : Xo + m0 * ldo;
-    rstride = rowbytes = (int)(2 * ldo);
-    rsrc = make_rsrc(seg_base, (uint32_t)op_rows_valid * (uint32_t)rowbytes);
-    set_offsets();
-    lds_barrier();   // every wave has read its factors
-    issue_pair(0);
-    issue_pair(2);
-    run_steps(rowbytes / BK, kF16);
+    if constexpr (!dense) {
+      const uint16_t* seg_base = loads_w ? Wo + n0 * ldo : Xo + m0 * ldo;
+      rstride = rowbytes = (int)(2 * ldo);
+      rsrc = make_rsrc(seg_base, (uint32_t)op_rows_valid * (uint32_t)rowbytes);
+      set_offsets();
+      lds_barrier();   // every wave has read its factors
+      issue_pair(0);
+      issue_pair(2);
+      run_steps(rowbytes / BK, kF16);
+    } else {
+      lds_barrier();   // every wave has read its factors
+      dense_segment();
+    }
     lds_barrier();
     store_scales();
   }
@@ -697,9 +865,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     load_fw(a, fw, bias ? bv : nullptr);
     v16f32 y[TM];
     if (seg2) {
-      // already dequantized, with the outlier product added
+      // already dequantized, with the outlier product added (dense: still
+      // without the factor sw/127)
 #pragma unroll
-      for (int b = 0; b < TM; ++b) y[b] = __builtin_bit_cast(v16f32, acc[a][b]);
+      for (int b = 0; b < TM; ++b) {
+        y[b] = __builtin_bit_cast(v16f32, acc[a][b]);
+        if (dense && Wf == nullptr) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[b][r] = y[b][r] * fw[r];
+        }
+      }
     } else {
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
@@ -736,23 +911,32 @@ template <class Cfg>
 hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                         const uint16_t* Wo, const uint16_t* Wf, hipStream_t s) {
-  const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+                         const uint16_t* Wo, int wo_cols, const uint16_t* Wf, const uint16_t* Xd,
+                         const uint32_t* bmp, hipStream_t s) {
+  const dim3 grid((unsigned)(((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN)));
+  const dim3 block(Cfg::THREADS);
   if (C) {
     // parity mode: the epilogue outlier path only
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
-                       Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, nullptr, Wf);
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M, (int)N,
+                       (int)K, Xo, cols, n_out, bias, Y, C, nullptr, 0, Wf, nullptr, nullptr);
     return hipGetLastError();
   }
-  // The outlier count is only known on the device: with Wo given both modes
-  // are launched and the one whose case it is not returns at once.
-  hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s, Xq,
-                     Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, Wf);
+  // The outlier count is only known on the device: with a second segment
+  // possible, its mode is launched too and the one whose case it is not
+  // returns at once.
+  hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M, (int)N,
+                     (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
   if (Wo) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, s,
-                       Xq, Wq, sx, sw, (int)M, (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, Wf);
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
+                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
+  }
+  if (Xd && bmp) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_i8<Cfg, kDenseSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
+                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
   }
   return hipGetLastError();
 }
@@ -772,7 +956,8 @@ constexpr int64_t kLargeTileMin = I8MM_LARGE_TILE_MIN;
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
-                       const uint16_t* Wo, const uint16_t* Wf, hipStream_t s) {
+                       const uint16_t* Wo, int wo_cols, const uint16_t* Wf,
+                       const uint16_t* Xd, const uint32_t* bmp, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   // (K == 0 goes to the tiled kernel, whose empty main loop leaves only the
   // epilogue: Y = bias, or 0)
@@ -782,8 +967,10 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
   // 128 x 128 tiles (four times as many, two blocks per CU).
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_large >= kLargeTileMin)
-    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, Wf, s);
-  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, Wf, s);
+    return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo,
+                                   wo_cols, Wf, Xd, bmp, s);
+  return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols,
+                                 Wf, Xd, bmp, s);
 }
 
 }  // namespace i8mm

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "i8mm.h"
+
 namespace i8mm {
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
@@ -44,27 +46,31 @@ hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uin
                               uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s);
 
 // Wo: the fp16 outlier weight columns [N, LD(n)] written by
-// launch_recover_outlier_w (or launch_gather_w_cols), or nullptr; with more
-// than 16 outlier columns and Wo given, the outlier product runs as a second
-// main-loop segment. Wf: the fp16 weight [N, K] when the layer keeps one
-// (its columns are the outlier weights), or nullptr (they are recovered from
-// Wq and sw).
+// launch_recover_outlier_w (or launch_gather_w_cols) with room for wo_cols
+// columns, or nullptr; with 16 < n <= wo_cols and Wo given, the outlier
+// product runs as a second main-loop segment over them. Xd, bmp: the
+// layer's X [M, K] and its outlier bitmap, or nullptr; given, more than 16
+// outlier columns that Wo does not take run as the dense second segment over
+// all K columns. Otherwise the outlier product runs in the epilogue. Wf: the
+// fp16 weight [N, K] when the layer keeps one (its columns are the outlier
+// weights), or nullptr (they are recovered from Wq and sw).
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
                        const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
-                       uint16_t* Y, int32_t* C, const uint16_t* Wo, const uint16_t* Wf,
+                       uint16_t* Y, int32_t* C, const uint16_t* Wo, int wo_cols,
+                       const uint16_t* Wf, const uint16_t* Xd, const uint32_t* bmp,
                        hipStream_t s);
 
 // Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)) for t < n, +0.0 up
-// to LD(n); nothing when n <= 16 (n read on the device).
+// to LD(n); nothing when n <= 16 or n > wo_cols (n read on the device).
 hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N, int64_t K,
-                                    const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
-                                    hipStream_t s);
+                                    const int32_t* cols, const int32_t* n_out, int wo_cols,
+                                    uint16_t* Wo, hipStream_t s);
 
 // Wo[j, t] = Wf[j, cols[t]] (the fp16 weight's own columns) for t < n, +0.0
-// up to LD(n); nothing when n <= 16 (n read on the device).
+// up to LD(n); nothing when n <= 16 or n > wo_cols (n read on the device).
 hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
-                                const int32_t* n_out, uint16_t* Wo, hipStream_t s);
+                                const int32_t* n_out, int wo_cols, uint16_t* Wo, hipStream_t s);
 
 // The whole layer in one launch for 1 <= M <= 16 tokens whose codes fit in
 // LDS (decode_applies): detection, row quantization and the few-token

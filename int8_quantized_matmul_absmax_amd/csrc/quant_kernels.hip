@@ -38,6 +38,7 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t val
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 
 // Per-column maximum of the fp16 magnitude patterns of a 16-byte chunk (8
 // columns), folded into mx[4] (element 2i in the low half of mx[i], 2i+1 in
@@ -405,6 +406,184 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   }
 }
 
+// Row pass of the layer (and of int8_quantize_rowwise with a bitmap) for
+// K <= 2048 * CPB. A block takes one row at a time, persistent over rows
+// blockIdx.x, blockIdx.x + gridDim.x, ...: thread t holds the 16-byte chunks
+// t, t + 256, ... (CPB of them), so a row costs a few registers per thread
+// and many waves stay resident. The next row's loads are issued before the
+// current row is worked on (two register sets). The outlier masks of a
+// thread's chunks are the same for every row and are taken once per block.
+// Per row: the outlier elements are gathered into Xo (rare), masked out, the
+// row absmax is a wave maximum (DPP) and one LDS exchange between the four
+// waves (one barrier per row; the exchange slots alternate between rows),
+// the codes are stored chunk by chunk. Loads and stores are buffer
+// operations over the row (the chunk offset in the scalar operand), so a
+// chunk past the row reads 0 and its store is dropped. Arithmetic as k_rows.
+template <int CPB, int FMODE>
+__global__ __launch_bounds__(256) void k_rows_flagged(
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ flags,
+    int bands, uint32_t* __restrict__ bitmap_out, int8_t* __restrict__ Xq,
+    float* __restrict__ sx, uint16_t* __restrict__ Xo, int32_t* __restrict__ cols,
+    int32_t* __restrict__ n_out) {
+  static_assert(CPB > 0 && CPB <= 8 && FMODE != kNoFlags, "flagged rows, K <= 16384");
+  extern __shared__ uint32_t smem[];
+  __shared__ int sred[kRowThreads / kWave];
+  __shared__ uint32_t s_max[2][kRowThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwords = (int)((K + 31) / 32);
+  const int64_t nchunks = K / 8;
+  uint32_t* sbm = smem;
+  uint32_t* spre = smem + nwords;
+  const int64_t row0 = blockIdx.x, rstep = gridDim.x;
+
+  // flag words first, then the first row: waiting for the flags leaves the
+  // row's loads in flight
+  constexpr int NFL = FMODE == kBands ? kMaxFlagBands : 1;
+  const int wi = tid < nwords ? tid : nwords - 1;
+  uint32_t fl[NFL];
+#pragma unroll
+  for (int b = 0; b < NFL; ++b) fl[b] = flags[(int64_t)(b < bands ? b : 0) * nwords + wi];
+  asm volatile("" ::: "memory");
+  const int voff_x = tid * 16;   // chunk t + 256 j: byte offset tid * 16 + j * 4096
+  auto load_row = [&](int64_t row, uint4 (&v)[CPB]) {
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(X + row * K, (uint32_t)(2 * K));
+#pragma unroll
+    for (int j = 0; j < CPB; ++j)
+      v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x, j * 4096, 0));
+  };
+  uint4 va[CPB], vb[CPB];
+  load_row(row0, va);   // row0 < M: the grid has at most M blocks
+
+  uint32_t fw = 0;
+#pragma unroll
+  for (int b = 0; b < NFL; ++b) fw |= fl[b];
+  sbm[wi] = fw;
+  for (int w = tid + kRowThreads; w < nwords; w += kRowThreads) {
+    uint32_t o = 0;
+    for (int b = 0; b < bands; ++b) o |= flags[(int64_t)b * nwords + w];
+    sbm[w] = o;
+  }
+  lds_only_barrier();   // LDS only: the first row's loads stay in flight
+  int n = 0;
+  if (Xo || cols || n_out) n = bitmap_prefix<true>(sbm, spre, nwords, sred);
+  if (blockIdx.x == 0) {
+    write_cols(sbm, spre, nwords, n, cols, n_out);
+    if (bitmap_out)
+      for (int w = tid; w < nwords; w += kRowThreads) bitmap_out[w] = sbm[w];
+  }
+  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
+
+  // outlier masks of the thread's chunks, four to a register (0 past the row)
+  constexpr int NPK = (CPB + 3) / 4;
+  uint32_t pk[NPK];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) pk[i] = 0;
+#pragma unroll
+  for (int j = 0; j < CPB; ++j) {
+    const int64_t c = tid + (int64_t)j * kRowThreads;
+    const int64_t k = c * 8;
+    const uint32_t om = c < nchunks ? (sbm[k >> 5] >> (k & 31)) & 0xffu : 0u;
+    pk[j / 4] |= om << (8 * (j % 4));
+  }
+  uint32_t any = 0;
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) any |= pk[i];
+  auto om_of = [&](int j) -> uint32_t { return (pk[j / 4] >> (8 * (j % 4))) & 0xffu; };
+  auto pick_half = [](const uint4& t, int e) -> uint32_t {
+    const uint32_t h = (uint32_t)(e & 3) * 2u;
+    const uint32_t sel = 0x0c0c0000u | ((h + 1u) << 8) | h;
+    const uint32_t p01 = __builtin_amdgcn_perm(t.y, t.x, sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(t.w, t.z, sel);
+    return (e & 4) ? p23 : p01;
+  };
+  const int voff_q = tid * 8;
+
+  auto process = [&](int64_t row, uint4 (&v)[CPB], int parity) {
+    // outlier elements: gathered into Xo from the unmodified chunk, then
+    // zeroed in it (a zero has magnitude 0 and code 0)
+    if (any) {
+#pragma unroll
+      for (int j = 0; j < CPB; ++j) {
+        const uint32_t om = om_of(j);
+        if (om) {
+          if (Xo) {
+            const int64_t k0 = (tid + (int64_t)j * kRowThreads) * 8;
+            int pos = (int)spre[k0 >> 5] + __popc(sbm[k0 >> 5] & ((1u << (k0 & 31)) - 1u));
+            uint16_t* dst = Xo + row * ld;
+            if (om == 0xffu && (pos & 7) == 0) {
+              st16(dst + pos, v[j]);   // 8 outlier columns at 8 aligned positions
+            } else {
+              for (uint32_t bits = om; bits; bits &= bits - 1u)
+                dst[pos++] = (uint16_t)pick_half(v[j], __builtin_ctz(bits));
+            }
+          }
+          uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] &= ((om >> (2 * i)) & 1u ? 0u : 0xffffu) |
+                    ((om >> (2 * i + 1)) & 1u ? 0u : 0xffff0000u);
+          v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+    // row absmax: thread, wave (DPP), then the four waves through LDS
+    u16x2 m2 = u16x2{0, 0};
+#pragma unroll
+    for (int j = 0; j < CPB; ++j) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+    }
+    const uint32_t mw = wave_max_u32_dpp(m2[0] > m2[1] ? m2[0] : m2[1]);
+    if (lane == 0) s_max[parity][wave] = mw;
+    lds_only_barrier();
+    uint32_t mx = s_max[parity][0];
+#pragma unroll
+    for (int w = 1; w < kRowThreads / kWave; ++w) mx = mx > s_max[parity][w] ? mx : s_max[parity][w];
+    const float a = h2f(mx);
+    const float sc = a != 0.0f ? 127.0f / a : 0.0f;
+    if (Xq) {
+      const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Xq + row * K, (uint32_t)K);
+#pragma unroll
+      for (int j = 0; j < CPB; ++j) {
+        const uint2 q = codes8_rne(v[j], sc);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, q), rq, voff_q, j * 2048, 0);
+      }
+      if (tid == 0) sx[row] = a;
+    }
+    if (Xo)
+      for (int64_t t = n + tid; t < ld; t += kRowThreads) Xo[row * ld + t] = 0;
+  };
+
+  // two rows per iteration, alternating register sets (static indices)
+  for (int64_t row = row0; row < M; row += 2 * rstep) {
+    const int64_t r1 = row + rstep;
+    if (r1 < M) load_row(r1, vb);
+    process(row, va, 0);
+    if (r1 >= M) break;
+    const int64_t r2 = r1 + rstep;
+    if (r2 < M) load_row(r2, va);
+    process(r1, vb, 1);
+  }
+}
+
+// Flagged row pass with the rows held across the block (K <= 2048 * CPB).
+template <int CPB>
+hipError_t launch_rows_flagged_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
+                                 int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
+                                 uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s) {
+  const int nwords = (int)((K + 31) / 32);
+  const size_t shm = (size_t)nwords * 2 * sizeof(uint32_t);
+  // four resident blocks per CU on 256 CUs; each block walks its rows
+  const int64_t blocks = std::min<int64_t>(M, 1024);
+  auto kern = bands == 1 ? k_rows_flagged<CPB, kBitmap> : k_rows_flagged<CPB, kBands>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K, flags,
+                     bands, bitmap_out, Xq, sx, Xo, cols, n_out);
+  return hipGetLastError();
+}
+
 template <int CPT>
 hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
                          int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx, uint16_t* Xo,
@@ -470,11 +649,11 @@ __device__ __forceinline__ void load_cols8(const int32_t* __restrict__ cols, int
 constexpr int kRecoverCols = 2048;   // columns per block and row: 256 threads x 8
 __global__ __launch_bounds__(kWoThreads) void k_recover_outlier_w(
     const int8_t* __restrict__ Wq, const float* __restrict__ sw, int64_t N, int64_t K,
-    const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
+    const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out, int wo_cols,
     uint16_t* __restrict__ Wo) {
   __shared__ uint16_t s_lut[130];   // q = 0..128 (-128 is a valid int8)
   const int n = *n_out;
-  if (n <= 16) return;
+  if (n <= 16 || n > wo_cols) return;   // the GEMM's other paths take those
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
   auto codes = [&](int64_t j, int64_t t0, int c[8], int q[8]) {
     load_cols8(cols, t0, n, c);
@@ -532,12 +711,13 @@ __global__ __launch_bounds__(kWoThreads) void k_recover_outlier_w(
 // Outlier weight columns of a layer that keeps its weight in fp16 ([HF-blog]
 // "Usage", has_fp16_weights=True): Wo[j, t] = W[j, cols[t]] as they are, for
 // t < n, +0.0 up to LD(n), with the same pieces as the recovery above.
-// Nothing when n <= 16 (the GEMM stages those itself).
+// Nothing when n <= 16 (the GEMM stages those itself) or n > wo_cols (the
+// region has no room: the GEMM's dense segment reads W itself).
 __global__ __launch_bounds__(kWoThreads) void k_gather_w_cols(
     const uint16_t* __restrict__ W, int64_t N, int64_t K, const int32_t* __restrict__ cols,
-    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Wo) {
+    const int32_t* __restrict__ n_out, int wo_cols, uint16_t* __restrict__ Wo) {
   const int n = *n_out;
-  if (n <= 16) return;
+  if (n <= 16 || n > wo_cols) return;   // the GEMM's other paths take those
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
   for_each_wo_piece(N, ld, [&](int64_t j, int64_t t0) {
     int c[8];
@@ -635,6 +815,18 @@ hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uin
                               int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
                               uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
+  if (flags && K > 0) {
+    // the block-per-row pass (chunks per thread: ceil(K / 2048))
+    const int64_t cpb = (K / 8 + kRowThreads - 1) / kRowThreads;
+#define I8MM_ROWSF(CPB) \
+  launch_rows_flagged_t<CPB>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, s)
+    if (cpb <= 1) return I8MM_ROWSF(1);
+    if (cpb <= 2) return I8MM_ROWSF(2);
+    if (cpb <= 4) return I8MM_ROWSF(4);
+    if (cpb <= 6) return I8MM_ROWSF(6);
+    if (cpb <= 8) return I8MM_ROWSF(8);
+#undef I8MM_ROWSF
+  }
   const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
 #define I8MM_ROWS(CPT) \
   launch_rows_t<CPT>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, s)
@@ -678,7 +870,8 @@ hipError_t launch_outlier_flag_bands(const uint16_t* X, int64_t M, int64_t K, ui
 }
 
 // Blocks for the Wo builders: n is only known on the device, so the grid is
-// sized for the largest n (K columns), at most 2048 blocks (a grid-stride
+// sized for the largest n that runs (K columns, or the region's room), at
+// most 2048 blocks (a grid-stride
 // loop covers the rest); blocks past the last piece exit at once.
 static unsigned wo_blocks(int64_t N, int64_t K) {
   const int64_t pieces = N * (I8MM_OUTLIER_LD(K) / 8);
@@ -686,19 +879,19 @@ static unsigned wo_blocks(int64_t N, int64_t K) {
 }
 
 hipError_t launch_recover_outlier_w(const int8_t* Wq, const float* sw, int64_t N, int64_t K,
-                                    const int32_t* cols, const int32_t* n_out, uint16_t* Wo,
-                                    hipStream_t s) {
-  if (N <= 0 || K <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_recover_outlier_w, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wq, sw,
-                     N, K, cols, n_out, Wo);
+                                    const int32_t* cols, const int32_t* n_out, int wo_cols,
+                                    uint16_t* Wo, hipStream_t s) {
+  if (N <= 0 || K <= 0 || wo_cols <= 16) return hipSuccess;
+  hipLaunchKernelGGL(k_recover_outlier_w, dim3(wo_blocks(N, std::min<int64_t>(K, wo_cols))),
+                     dim3(kWoThreads), 0, s, Wq, sw, N, K, cols, n_out, wo_cols, Wo);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_w_cols(const uint16_t* Wf, int64_t N, int64_t K, const int32_t* cols,
-                                const int32_t* n_out, uint16_t* Wo, hipStream_t s) {
-  if (N <= 0 || K <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather_w_cols, dim3(wo_blocks(N, K)), dim3(kWoThreads), 0, s, Wf, N, K,
-                     cols, n_out, Wo);
+                                const int32_t* n_out, int wo_cols, uint16_t* Wo, hipStream_t s) {
+  if (N <= 0 || K <= 0 || wo_cols <= 16) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_w_cols, dim3(wo_blocks(N, std::min<int64_t>(K, wo_cols))),
+                     dim3(kWoThreads), 0, s, Wf, N, K, cols, n_out, wo_cols, Wo);
   return hipGetLastError();
 }
 

@@ -19,11 +19,37 @@ holding CB and SCB under those names, and through the module's state dict,
 whose extra state records that the buffers hold a quantized weight.
 """
 
+import threading
+
 import torch
 
 from . import ops
 
 INT8_FORMAT = "llm-int8/per-output-row-absmax/v1"
+
+# One workspace per (device, stream), shared by every module: the layers of a
+# model run one after another on a stream, so they can share their scratch
+# (outlier flags and columns, row scales, int8 codes, gathered outlier
+# activations, and the region of recovered outlier weights, room for 512
+# columns per output row). A model then holds one layer's worth of
+# workspace, not one per module. Calls on different streams get their own.
+# Each call takes the prefix of the layer's own size, so the layer's path
+# (and its result bits) do not depend on which layers ran before.
+_WS_LOCK = threading.Lock()
+_WORKSPACES = {}
+
+
+def shared_workspace(device, nbytes):
+    """The shared workspace of the current stream on `device`, grown to at
+    least nbytes (uint8 tensor)."""
+    device = torch.device(device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    with _WS_LOCK:
+        ws = _WORKSPACES.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+            _WORKSPACES[key] = ws
+        return ws
 
 
 def save_int8_weight(path, Wq, sw, bias=None, threshold=ops.DEFAULT_THRESHOLD):
@@ -95,7 +121,6 @@ class Int8Linear(torch.nn.Module):
         self.requantize_every_call = True
         self._quantized = False     # int8 mode: weight quantized; fp16 mode: weight set
         self._codes_current = False
-        self._ws = None
 
     @property
     def CB(self):
@@ -154,14 +179,13 @@ class Int8Linear(torch.nn.Module):
             raise TypeError("input must be fp16")
         x = x.contiguous()
         M = x.numel() // self.in_features
-        need = ops.workspace_bytes(M, self.in_features, self.out_features)
-        if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
-            self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        nbytes = ops.workspace_bytes(M, self.in_features, self.out_features)
+        ws = shared_workspace(x.device, nbytes)[:nbytes]
         if not self.has_fp16_weights:
-            return ops.linear_int8_mixed(x, self.Wq, self.sw, self.bias, self.threshold, self._ws)
+            return ops.linear_int8_mixed(x, self.Wq, self.sw, self.bias, self.threshold, ws)
         requantize = self.requantize_every_call or not self._codes_current
         Y = ops.linear_int8_mixed_fp16_weights(x, self.weight, self.Wq, self.sw, requantize,
-                                               self.bias, self.threshold, self._ws)
+                                               self.bias, self.threshold, ws)
         if M > 0:
             self._codes_current = True
         return Y

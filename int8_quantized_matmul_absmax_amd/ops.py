@@ -198,12 +198,32 @@ def int8_mm_dequant(Xq, Wq, sx, sw, Xo=None, cols=None, n=None, bias=None, want_
 
 def workspace_bytes(M, K, N=None):
     """Workspace bytes of linear_int8_mixed for M tokens and K features; with N
-    (output features) given, the size that also enables the fast path for
-    many outlier columns."""
+    (output features) given, the size with a region of recovered outlier
+    weights with room for 512 columns, which speeds up 17 to 512 outlier
+    columns; without it every outlier count still takes a second GEMM loop.
+    Any larger workspace has room for floor(extra / (2 N) / 32) * 32 columns
+    (see workspace_bytes_all_outliers)."""
     lib = _lib.load_library()
     if N is None:
         return int(lib.linear_int8_mixed_workspace_bytes(int(M), int(K)))
     return int(lib.linear_int8_mixed_workspace_bytes_many_outliers(int(M), int(K), int(N)))
+
+
+def workspace_bytes_all_outliers(M, K, N):
+    """Workspace bytes whose outlier weight region has room for every outlier
+    count (K columns): the fastest layer at any count, for N * outlier_ld(K)
+    * 2 extra bytes."""
+    base = workspace_bytes(M, K)
+    return base + int(N) * outlier_ld(int(K)) * 2 if base else 0
+
+
+def outlier_region_cols(workspace_bytes_, M, K, N):
+    """Outlier columns a workspace of workspace_bytes_ bytes has room for in
+    its recovered-weight region (0 means none)."""
+    extra = int(workspace_bytes_) - workspace_bytes(M, K)
+    if extra <= 0 or N <= 0:
+        return 0
+    return min(extra // (2 * int(N)) // 32 * 32, outlier_ld(int(K)))
 
 
 def workspace_layout(M, K):
@@ -289,12 +309,15 @@ def gelu_f16(X, out=None):
     return Y
 
 
+OUTLIER_REGION_COLS = 512   # I8MM_OUTLIER_REGION_COLS
+
+
 def workspace_views(workspace, M, K, N=None):
     """Typed views of the intermediates inside a linear_int8_mixed workspace.
-    Given N and a workspace of workspace_bytes(M, K, N), also "Wo": the fp16
-    outlier weight columns the tiled path materializes with more than 16
-    outlier columns, N rows outlier_ld(n) halfs apart (flat, capacity
-    N * outlier_ld(K))."""
+    Given N and a workspace larger than workspace_bytes(M, K), also "Wo": the
+    region of fp16 outlier weight columns the tiled path materializes when
+    16 < n <= outlier_region_cols(...), N rows outlier_ld(n) halfs apart
+    (flat, the region's whole room)."""
     off = workspace_layout(M, K)
     w = workspace
     views = {
@@ -306,8 +329,9 @@ def workspace_views(workspace, M, K, N=None):
         "Xo": w[off["Xo"]:off["Xo"] + M * outlier_ld(K) * 2].view(torch.float16),
     }
     if N is not None:
-        end = off["total"] + int(N) * outlier_ld(K) * 2
-        if workspace.numel() < end:
+        room = outlier_region_cols(workspace.numel(), M, K, N)
+        if room == 0:
             raise ValueError("workspace has no outlier weight region for N=%d" % N)
+        end = off["total"] + int(N) * room * 2
         views["Wo"] = w[off["total"]:end].view(torch.float16)
     return views

@@ -74,6 +74,37 @@ def test_workspace_layout_is_pure_and_consistent(lib):
     assert lib.i8mm_workspace_layout(4, 16, None) == _lib.I8MM_EINVAL
 
 
+def test_many_outlier_region_is_capped(lib):
+    """The optional region of recovered outlier weights holds at most
+    I8MM_OUTLIER_REGION_COLS (512) columns per output row, whatever K: its
+    memory is bounded by N x 1 KiB, not N x K halfs."""
+    assert i8.ops.OUTLIER_REGION_COLS == 512
+    for M, K, N in [(16, 256, 100), (2048, 4096, 16384), (4096, 12288, 49152), (1024, 16384, 4096)]:
+        base = lib.linear_int8_mixed_workspace_bytes(M, K)
+        big = lib.linear_int8_mixed_workspace_bytes_many_outliers(M, K, N)
+        cols = min(K, 512)
+        region = N * ((cols + 31) // 32 * 32) * 2
+        assert big - base == (region + 255) // 256 * 256
+    assert lib.linear_int8_mixed_workspace_bytes_many_outliers(16, 4096, -1) == 0
+
+
+def test_outlier_region_room():
+    """The room of the recovered-weight region is what the extra bytes hold,
+    in whole 32-column groups, at most LD(K): the default region has room for
+    512 columns (K >= 512), the all-outliers size for every count, and a
+    region one byte short of a group loses that group."""
+    ops = i8.ops
+    for M, K, N in [(16, 256, 100), (2048, 4096, 16384), (300, 2064, 4100), (1, 16, 1)]:
+        base = ops.workspace_bytes(M, K)
+        assert ops.outlier_region_cols(base, M, K, N) == 0
+        assert ops.outlier_region_cols(ops.workspace_bytes(M, K, N), M, K, N) == \
+            min(512, ops.outlier_ld(K))
+        assert ops.outlier_region_cols(ops.workspace_bytes_all_outliers(M, K, N), M, K, N) == \
+            ops.outlier_ld(K)
+        assert ops.outlier_region_cols(base + 64 * N - 1, M, K, N) == 0
+        assert ops.outlier_region_cols(base + 64 * N, M, K, N) == min(32, ops.outlier_ld(K))
+
+
 def test_validation_quantize_weight(lib):
     f = lib.int8_quantize_colwise_weight
     assert f(NUL, 4, 16, A, A2, NUL) == _lib.I8MM_EINVAL

@@ -1,6 +1,7 @@
 """The single-launch few-token layer: the layer calls take it for M <= 8
 tokens with K <= 16384 (M <= 4) or 8192 (M <= 8), the columns of X a thread
-holds in registers; 9 to 64 tokens take the separate kernels (also here).
+holds in registers; other few-token shapes (up to 64 tokens) take the
+separate kernels (also here).
 
 Against the oracle: every intermediate it writes to the workspace bit for
 bit (bitmap, cols, n, codes, scales, gathered outlier columns and their zero
@@ -32,11 +33,15 @@ CASES = {
     "m5_k2064": (5, 2064, 300, 3, False, False),
     "m8_k8192_n40": (8, 8192, 257, 40, True, False),
     "m9_k1040_separate": (9, 1040, 100, 20, False, False),
+    "m12_k2048_n40_separate": (12, 2048, 130, 40, True, False),
+    "m16_k4112_separate": (16, 4112, 200, 7, False, False),
     "m8_k4096_many_tiles": (8, 4096, 16400, 6, True, False),
+    "m16_k4096_many_tiles_separate": (16, 4096, 16400, 6, True, False),
     "m3_k16": (3, 16, 64, 0, False, False),
     "m7_fp16w": (7, 4096, 300, 8, True, True),
     "m16_fp16w_separate": (16, 4096, 300, 8, True, True),
     "m2_fp16w_n33": (2, 4112, 333, 33, False, True),
+    "m20_fp16w_separate": (20, 4096, 300, 8, True, True),
 }
 
 

@@ -86,6 +86,7 @@ CASES = {
     "gemm_small_n50_big_ws": (97, 2064, 520, 50, True, True),
     "gemm_large_n9": (4100, 528, 4100, 9, True, False),
     "gemm_large_n40_big_ws": (4100, 528, 4100, 40, False, True),
+    "gemm_large_n40": (4100, 528, 4100, 40, True, False),
 }
 
 
@@ -109,18 +110,21 @@ def test_fp16_weights_layer(gpu, case):
 
 
 @pytest.mark.parametrize("M", [40, 300])
-def test_fp16_weights_fast_and_slow_paths_agree(gpu, M):
-    """More than 16 outlier columns: the larger workspace gathers W's columns
-    and runs the outlier product as a second main loop (tiled GEMM); the
-    smaller one adds the same products in the same order in the epilogue. The
-    few-token path ignores the region. Bit-identical either way."""
-    note("fp16 weights fast/slow M=%d" % M)
+def test_fp16_weights_both_workspaces(gpu, M):
+    """More than 16 outlier columns: with the region, the tiled path gathers
+    W's columns and runs the outlier product as a second loop over them; the
+    minimal workspace takes the dense loop over all K columns with W's own
+    fp16 values (normal columns zeroed). The few-token path ignores the
+    region (bit-identical either way). Both within the tolerance."""
+    note("fp16 weights both workspaces M=%d" % M)
     X, W, b = _inputs(700 + M, M, 1040, 330, 33, True)
     ref = O.linear_int8_mixed_fp16_weights(X, W, 6.0, b)
     Y_big, _, _, _ = _run(gpu, X, W, 6.0, b, True)
     Y_small, _, _, _ = _run(gpu, X, W, 6.0, b, False)
     assert y_err(Y_big, ref["Y"]) <= Y_TOL
-    assert np.array_equal(Y_big.view(np.uint16), Y_small.view(np.uint16))
+    assert y_err(Y_small, ref["Y"]) <= Y_TOL
+    if M <= 64:
+        assert np.array_equal(Y_big.view(np.uint16), Y_small.view(np.uint16))
 
 
 @pytest.mark.parametrize("M", [8, 200])

@@ -284,19 +284,23 @@ def test_linear_edge_cases(gpu, case):
 
 
 @pytest.mark.parametrize("case", ["n17", "n33", "n70", "n100", "all_columns", "large_tiles_n40",
-                                  "large_tiles_all", "wide_all"])
-def test_linear_many_outliers_fast_path(gpu, case):
-    """More than 16 outlier columns with the larger workspace: the recovered
-    outlier weights are materialized and the outlier product runs as a second
-    GEMM main loop (all columns outliers: the int8 loop is skipped). Checked
-    against the oracle, and bit for bit against the small-workspace path,
-    which adds the same fp16 MFMA products in the same order in the epilogue.
-    wide_all: N * LD(K) / 8 = 1.07M 16-byte pieces of recovered weights,
-    more than the recovery's grid covers in one pass."""
+                                  "large_tiles_all", "wide_all", "n600"])
+def test_linear_many_outliers(gpu, case):
+    """More than 16 outlier columns, three workspaces: the minimal one, the
+    default region of recovered weights (workspace_bytes(M, K, N), room for
+    512 columns) and a region with room for every count
+    (workspace_bytes_all_outliers). With room for the n columns the recovered
+    weights are materialized, bit for bit against the oracle, and the outlier
+    product runs as a second GEMM loop over them; its Y is bit-identical to
+    the step call's, which adds the same fp16 MFMA products in the same order
+    in the epilogue. Without room the GEMM's dense second loop runs over all
+    K columns (all columns outliers: the int8 loop is skipped). Every Y within
+    the tolerance of the oracle. wide_all: N * LD(K) / 8 = 1.07M 16-byte
+    pieces, more than one pass of the recovery's grid."""
     note("linear many outliers %s" % case)
     rng = np.random.default_rng(300 + len(case))
     large = case.startswith("large_tiles")
-    M, K, N = (4100, 528, 4100) if large else (300, 2064, 4100) if case == "wide_all" \
+    M, K, N = (4100, 528, 4100) if large else (300, 2064, 4100) if case in ("wide_all", "n600") \
         else (200, 1040, 300)
     X = synth.normal_f16(rng, (M, K), 1.0)
     W = synth.normal_f16(rng, (N, K), 0.05)
@@ -311,22 +315,85 @@ def test_linear_many_outliers_fast_path(gpu, case):
     ref = O.linear_int8_mixed(X, Wq, sw, tau, bias)
     assert ref["n"] > 16
     ops = _ops(gpu)
+    ws_all = torch.empty((ops.workspace_bytes_all_outliers(M, K, N),), dtype=torch.uint8,
+                         device="cuda")
     ws_big = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
     ws_small = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    assert ops.outlier_region_cols(ws_all.numel(), M, K, N) == ops.outlier_ld(K)
     Xd, Wqd, swd, bd = dev(X), dev(Wq), dev(sw), dev(bias)
-    Y_fast = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_big)
-    Y_slow = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_small)
+    Y_big = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_big)
+    Y_small = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_small)
+    Y_all = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_all)
     torch.cuda.synchronize()
-    views = ops.workspace_views(ws_big, M, K, N)
+    views = ops.workspace_views(ws_all, M, K, N)
     _check_intermediates(gpu, views, X, ref)
+    for Y in (Y_big, Y_small, Y_all):
+        assert y_err(host(Y), ref["Y"]) <= Y_TOL
     # the recovered weights, bit for bit, and their zero pad
     n, ld = ref["n"], ops.outlier_ld(ref["n"])
     Wo = host(views["Wo"])[: N * ld].reshape(N, ld).view(np.uint16)
     Wo_ref = O.recover_outlier_weights(Wq, sw, ref["cols"]).view(np.uint16)
     assert np.array_equal(Wo[:, :n], Wo_ref)
     assert not Wo[:, n:].any()
-    assert y_err(host(Y_fast), ref["Y"]) <= Y_TOL
-    assert np.array_equal(host(Y_fast).view(np.uint16), host(Y_slow).view(np.uint16))
+    Y_step = ops.int8_mm_dequant(views["Xq"], Wqd, views["sx"], swd, views["Xo"],
+                                 views["cols"], views["n"], bd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Y_all).view(np.uint16), host(Y_step).view(np.uint16))
+    if n <= ops.OUTLIER_REGION_COLS:
+        assert np.array_equal(host(Y_big).view(np.uint16), host(Y_step).view(np.uint16))
+    else:
+        # no room for that many in the default region: it takes the dense
+        # loop, as the minimal workspace does
+        assert np.array_equal(host(Y_big).view(np.uint16), host(Y_small).view(np.uint16))
+
+
+@pytest.mark.parametrize("case", ["clustered", "ragged_k", "sparse_words", "small_tiles_all",
+                                  "large_tiles_600"])
+def test_linear_dense_outlier_loop(gpu, case):
+    """The GEMM's dense second loop (the workspace without the region of
+    recovered weights): outlier columns clustered in a few 32-column words
+    (the other words' stages issue no MFMA), K with a half-empty last stage
+    (K % 32 == 16), outlier columns spread one per word, every column an
+    outlier on the 128 x 128 tiles, and 600 columns on the 256 x 256 tiles
+    with ragged M and N. Intermediates bit for bit, Y within the tolerance;
+    with the int32 step call, the accumulators of the normal part bit for
+    bit."""
+    note("dense outlier loop %s" % case)
+    rng = np.random.default_rng(640 + len(case))
+    M, K, N = {"clustered": (300, 2048, 700), "ragged_k": (200, 1040, 330),
+               "sparse_words": (130, 2048, 260), "small_tiles_all": (256, 1024, 384),
+               "large_tiles_600": (4100, 2064, 4100)}[case]
+    X = np.clip(synth.normal_f16(rng, (M, K), 1.0).astype(np.float32), -5.0, 5.0).astype(np.float16)
+    tau = 6.0
+    if case == "clustered":
+        cols = np.concatenate([np.arange(64, 96), np.arange(1000, 1010), np.arange(2040, 2048)])
+    elif case == "ragged_k":
+        cols = np.concatenate([np.arange(0, 20), np.arange(1030, 1040)])
+    elif case == "sparse_words":
+        cols = np.arange(5, K, 32)
+    elif case == "small_tiles_all":
+        cols, tau = np.arange(K), 0.0
+    else:
+        cols = np.sort(rng.choice(K, 600, replace=False))
+    for c in cols:
+        rows = rng.choice(M, size=max(1, M // 4), replace=False)
+        X[rows, c] = (rng.uniform(7.0, 40.0, rows.size) * rng.choice([-1.0, 1.0], rows.size)).astype(np.float16)
+    W = synth.normal_f16(rng, (N, K), 0.05)
+    bias = synth.normal_f16(rng, (N,), 0.5)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, tau, bias)
+    if tau > 0:
+        assert ref["cols"].tolist() == sorted(cols.tolist())
+    Y, views = _run_linear(gpu, X, Wq, sw, tau, bias)
+    _check_intermediates(gpu, views, X, ref)
+    err = y_err(Y, ref["Y"])
+    assert err <= Y_TOL, err
+    ops = _ops(gpu)
+    C = ops.int8_mm_dequant(views["Xq"], dev(Wq), views["sx"], dev(sw), want_y=False,
+                            want_int32=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 64, 7)
+    assert np.array_equal(host(C)[rows], O.int32_accumulators(ref["Xq"][rows], Wq))
 
 
 def test_linear_large_tiles_ragged(gpu):
@@ -623,3 +690,33 @@ def test_outlier_detect_quantize(gpu, shape):
     # few-token path too, whose single launch matches the separate kernels)
     assert np.array_equal(host(Y).view(np.uint16), Y_l.view(np.uint16))
     assert lay["total"] == ops.workspace_bytes(M, K)
+
+
+def test_int8_linear_modules_share_one_workspace(gpu):
+    """Modules of different shapes, called in turn on one stream, use one
+    shared workspace (grown to the largest need) and each output is the
+    oracle's."""
+    note("Int8Linear shared workspace")
+    from int8_quantized_matmul_absmax_amd import linear as L
+    rng = np.random.default_rng(88)
+    shapes = [(512, 96, 40), (1040, 300, 130), (512, 64, 7)]   # (in, out, tokens)
+    mods, refs, xs = [], [], []
+    for k, n, m in shapes:
+        W = synth.normal_f16(rng, (n, k), 0.05)
+        X = synth.normal_f16(rng, (m, k), 1.0)
+        synth.plant_outlier_columns(rng, X, 20, 7.0, 30.0, 0.5)
+        lin = gpu.Int8Linear(k, n)
+        lin.quantize_(dev(W))
+        Wq, sw = O.quantize_weight_rows(W)
+        mods.append(lin)
+        refs.append(O.linear_int8_mixed(X, Wq, sw, 6.0)["Y"])
+        xs.append(dev(X))
+    for _ in range(2):
+        for lin, X, ref in zip(mods, xs, refs):
+            Y = host(lin(X))
+            assert y_err(Y, ref) <= Y_TOL
+    key = (torch.device("cuda").index or 0, torch.cuda.current_stream().cuda_stream)
+    ws = L._WORKSPACES[key]
+    need = max(gpu.ops.workspace_bytes(m, k, n) for k, n, m in shapes)
+    assert ws.numel() >= need
+    assert sum(1 for (dev_i, _) in L._WORKSPACES if dev_i == key[0]) >= 1

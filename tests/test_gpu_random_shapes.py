@@ -11,9 +11,11 @@ builders and the GEMM's pick-up of outlier weight codes, at ragged sizes.
 Two more cases use the large GEMM tiles (2100 x 8200 outputs).
 
 Against the oracle: the intermediates bit for bit and Y within the
-tolerance; with the larger workspace, Y also bit for bit against the
-smaller one (the two outlier-product paths add the same products in the
-same order).
+tolerance, with either workspace. With at most 16 outlier columns, or on
+the few-token paths (which do not use the region), the two workspaces give
+the same Y bits; with more columns the tiled GEMM runs the outlier product
+over the recovered weights with the region and as its dense loop over all
+columns without it (different fp32 sums), each checked against the oracle.
 """
 
 import numpy as np
@@ -76,4 +78,7 @@ def test_random_shape(gpu, seed):
         ws_small = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
         Y2 = ops.linear_int8_mixed(Xd, Wqd, swd, bd, tau, ws_small)
         torch.cuda.synchronize()
-        assert np.array_equal(host(Y).view(np.uint16), host(Y2).view(np.uint16))
+        err2 = y_err(host(Y2), ref["Y"])
+        assert err2 <= Y_TOL, err2
+        if ref["n"] <= 16 or M <= 64:
+            assert np.array_equal(host(Y).view(np.uint16), host(Y2).view(np.uint16))
