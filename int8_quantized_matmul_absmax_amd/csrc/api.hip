@@ -11,7 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/i8mm.h"
+#include "i8mm.h"
 #include "launchers.h"
 
 namespace {
