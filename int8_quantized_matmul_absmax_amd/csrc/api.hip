@@ -86,8 +86,10 @@ constexpr int64_t kAlign = 256;
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // Workspace of linear_int8_mixed: bitmap | cols | n | sx | Xq | Xo |
-// partial flag words (kMaxFlagBands x ceil(K/32), at *part when given).
-bool layout(int64_t M, int64_t K, int64_t* off, int64_t* part = nullptr) {
+// partial flag words (kMaxFlagBands x ceil(K/32), at *part when given) |
+// the GEMM's k-block list (1 + ceil(K/64) ints, at *kbl when given).
+bool layout(int64_t M, int64_t K, int64_t* off, int64_t* part = nullptr,
+            int64_t* kbl = nullptr) {
   if (M < 0 || K < 0 || K % 16 != 0 || K > I8MM_MAX_K || M > INT32_MAX) return false;
   int64_t p = 0;
   off[0] = p; p = round_up(p + (K + 31) / 32 * 4, kAlign);
@@ -98,6 +100,8 @@ bool layout(int64_t M, int64_t K, int64_t* off, int64_t* part = nullptr) {
   off[5] = p; p = round_up(p + M * I8MM_OUTLIER_LD(K) * 2, kAlign);
   if (part) *part = p;
   p = round_up(p + i8mm::kMaxFlagBands * ((K + 31) / 32) * 4, kAlign);
+  if (kbl) *kbl = p;
+  p = round_up(p + (1 + (K + 63) / 64) * 4, kAlign);
   off[6] = p;
   return true;
 }
@@ -224,7 +228,7 @@ int int8_mm_dequant(const int8_t* Xq, const int8_t* Wq, const float* sx, const f
   hipStream_t s = (hipStream_t)stream;
   I8MM_TRY(launched(
       i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_outliers, bias, Y, C, nullptr, 0,
-                        nullptr, nullptr, nullptr, s),
+                        nullptr, nullptr, nullptr, nullptr, s),
       fn));
   return ok();
 }
@@ -235,10 +239,11 @@ namespace {
 
 // The activation side of the layer (steps a1-a3) into the workspace:
 // detection as per-band partial flags (no clearing launch), then the row
-// pass, which ORs them, writes the bitmap, cols and n, gathers the outlier
-// columns into Xo and quantizes the normal part into Xq, sx.
+// pass, which ORs them, writes the bitmap, cols, n and the GEMM's k-block
+// list, gathers the outlier columns into Xo and quantizes the normal part
+// into Xq, sx.
 int x_side(const char* fn, const uint16_t* X, int64_t M, int64_t K, uint32_t tau16, char* ws,
-           const int64_t* off, int64_t off_part, hipStream_t s) {
+           const int64_t* off, int64_t off_part, int64_t off_kbl, hipStream_t s) {
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + off[0]);
   int32_t* cols = reinterpret_cast<int32_t*>(ws + off[1]);
   int32_t* n_o = reinterpret_cast<int32_t*>(ws + off[2]);
@@ -246,10 +251,12 @@ int x_side(const char* fn, const uint16_t* X, int64_t M, int64_t K, uint32_t tau
   int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
   uint16_t* Xo = reinterpret_cast<uint16_t*>(ws + off[5]);
   uint32_t* part = reinterpret_cast<uint32_t*>(ws + off_part);
+  int32_t* kbl = reinterpret_cast<int32_t*>(ws + off_kbl);
   const int bands = i8mm::flag_bands(M, K);
   I8MM_TRY(launched(i8mm::launch_outlier_flag_bands(X, M, K, tau16, bands, part, s), fn));
   I8MM_TRY(launched(
-      i8mm::launch_rows_banded(X, M, K, part, bands, bitmap, Xq, sx, Xo, cols, n_o, s), fn));
+      i8mm::launch_rows_banded(X, M, K, part, bands, bitmap, Xq, sx, Xo, cols, n_o, kbl, s),
+      fn));
   return I8MM_OK;
 }
 
@@ -280,8 +287,8 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
   I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
   I8MM_TRY(check_ptr(fn, "bias", bias, false));
   I8MM_TRY(check_ptr(fn, "Y", Y, M * N > 0));
-  int64_t off[7], off_part = 0;
-  layout(M, K, off, &off_part);
+  int64_t off[7], off_part = 0, off_kbl = 0;
+  layout(M, K, off, &off_part, &off_kbl);
   I8MM_TRY(check_workspace(fn, workspace, workspace_bytes, off));
   if (M == 0 || N == 0) return ok();
   I8MM_TRY(check_device());
@@ -304,7 +311,7 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
                       fn));
     return ok();
   }
-  I8MM_TRY(x_side(fn, X, M, K, tau16, ws, off, off_part, s));
+  I8MM_TRY(x_side(fn, X, M, K, tau16, ws, off, off_part, off_kbl, s));
   // The workspace beyond the minimal layout holds the recovered fp16 outlier
   // weight columns for the tiled GEMM, N rows of LD(n) halfs, for n up to the
   // columns it has room for (the kernels do nothing for 16 or fewer columns,
@@ -324,7 +331,8 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
     }
   }
   I8MM_TRY(launched(i8mm::launch_gemm(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_o, bias, Y, nullptr,
-                                      Wo, wo_cols, Wf, X, bitmap, s),
+                                      Wo, wo_cols, Wf, X, bitmap,
+                                      reinterpret_cast<const int32_t*>(ws + off_kbl), s),
                     fn));
   return ok();
 }
@@ -357,13 +365,13 @@ int outlier_detect_quantize(const uint16_t* X, int64_t M, int64_t K, float thres
   I8MM_TRY(check_dims(fn, M, 0, K));
   if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
   I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
-  int64_t off[7], off_part = 0;
-  layout(M, K, off, &off_part);
+  int64_t off[7], off_part = 0, off_kbl = 0;
+  layout(M, K, off, &off_part, &off_kbl);
   I8MM_TRY(check_workspace(fn, workspace, workspace_bytes, off));
   if (M == 0) return ok();
   I8MM_TRY(check_device());
   I8MM_TRY(x_side(fn, X, M, K, i8mm::fp16_threshold_pattern(threshold),
-                  static_cast<char*>(workspace), off, off_part, (hipStream_t)stream));
+                  static_cast<char*>(workspace), off, off_part, off_kbl, (hipStream_t)stream));
   return ok();
 }
 

@@ -178,4 +178,33 @@ __device__ inline void write_cols(const uint32_t* sbm, const uint32_t* spre, int
   if (n_out && threadIdx.x == 0) *n_out = n;
 }
 
+// The 64-column k-blocks that hold at least one normal (non-outlier) column:
+// kbl[0] = their count, kbl[1 ..] = their indices, ascending. Columns past K
+// count as outlier columns. The int8 GEMM visits only these blocks when many
+// columns are outliers (an all-outlier block has only zero codes). Wave 0 of
+// the block, 64 k-blocks per pass; sbm holds the bitmap.
+__device__ inline void write_kblocks(const uint32_t* sbm, int64_t K, int32_t* __restrict__ kbl) {
+  if (!kbl || threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int nkb = (int)((K + 63) / 64);
+  int base = 0;
+  for (int kb0 = 0; kb0 < nkb; kb0 += kWave) {
+    const int kb = kb0 + lane;
+    bool act = false;
+    if (kb < nkb) {
+      const int valid = (int)(K - (int64_t)kb * 64 < 64 ? K - (int64_t)kb * 64 : 64);
+      const uint32_t m0 = valid >= 32 ? 0xffffffffu : (1u << valid) - 1u;
+      act = (sbm[2 * kb] & m0) != m0;
+      if (valid > 32) {
+        const uint32_t m1 = valid >= 64 ? 0xffffffffu : (1u << (valid - 32)) - 1u;
+        act = act || (sbm[2 * kb + 1] & m1) != m1;
+      }
+    }
+    const uint64_t b = __ballot(act);
+    if (act) kbl[1 + base + __popcll(b & ((1ull << lane) - 1ull))] = kb;
+    base += __popcll(b);
+  }
+  if (lane == 0) kbl[0] = base;
+}
+
 }  // namespace i8mm

@@ -186,7 +186,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int32_t* __restrict__ cols, const int32_t* __restrict__ n_out,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C,
     const uint16_t* __restrict__ Wo, int wo_cols, const uint16_t* __restrict__ Wf,
-    const uint16_t* __restrict__ Xd, const uint32_t* __restrict__ bmp) {
+    const uint16_t* __restrict__ Xd, const uint32_t* __restrict__ bmp,
+    const int32_t* __restrict__ kbl) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN, KS = Cfg::KS;
   constexpr int LOADS = Cfg::LOADS, RPL = Cfg::ROWS_PER_LOAD;
@@ -343,9 +344,28 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
   set_offsets();
-  // Wave-wide load j of stage kt (LOADS per wave per stage).
-  auto issue_load = [&](int kt, int j) {
-    const int k0 = kt * BK;
+  // The k-blocks the int8 loop visits. In the segment modes, given the list
+  // the row pass writes (kbl[0] = count, then the k-blocks that hold at least
+  // one normal column, ascending), only those: a k-block of outlier columns
+  // has all-zero codes. Otherwise all of them (none with every column an
+  // outlier column). Stage kt holds k-block kmap(kt); past the last visited
+  // stage, kmap gives a k-block past K, whose loads read zeros.
+  static_assert(BK == 64, "the k-block list is in 64-column blocks");
+  const int nkb_all = (K + BK - 1) / BK;
+  bool list_on = seg2 && kbl != nullptr;
+  const int nk = list_on ? __builtin_amdgcn_readfirstlane(kbl[0])
+                         : ((seg2 && n_o == K) ? 0 : nkb_all);
+  auto kmap = [&](int kt) -> int {
+    if constexpr (!seg2) {
+      return kt;
+    } else {
+      if (!list_on) return kt;
+      return kt < nk ? __builtin_amdgcn_readfirstlane(kbl[1 + kt]) : nkb_all;
+    }
+  };
+  // Wave-wide load j of stage kt, k-block kb (LOADS per wave per stage).
+  auto issue_load = [&](int kt, int kb, int j) {
+    const int k0 = kb * BK;
     int8_t* sbase = stages + (kt % STAGES) * Cfg::STAGE_BYTES + row_first * BK;
     const int soff = __builtin_amdgcn_readfirstlane((j & ~1) * RPL * rstride + k0);
     const bool ok = k0 < kleft[j & 1] && (j & ~1) * RPL < rleft[j & 1];
@@ -354,10 +374,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
                                              soff, 0, 0);
   };
   auto issue_pair = [&](int kt) {   // stages kt, kt + 1, row block by row block
+    const int kb0 = kmap(kt), kb1 = kmap(kt + 1);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      issue_load(kt, j);
-      issue_load(kt + 1, j);
+      issue_load(kt, kb0, j);
+      issue_load(kt + 1, kb1, j);
     }
   };
 
@@ -446,6 +467,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // gained nothing.
   constexpr int PRE = Cfg::WAVES_M == 4 ? Cfg::NMFMA / 4 : 0;
   constexpr int NM = Cfg::NMFMA;
+  // k-blocks of the pair of stages the current two steps load (pkb) and of
+  // the next pair (npkb, looked up one step ahead so the scalar loads of the
+  // list have landed when the loads need them)
+  int pkb0 = 0, pkb1 = 0, npkb0 = 0, npkb1 = 0;
   auto step = [&](int k, int set, auto f16) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < PRE; ++m) mfma_one(m, set, f16);
@@ -457,9 +482,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int8_t* rbase = stages + ((k + 1) % STAGES) * Cfg::STAGE_BYTES;
     const int pair0 = set == 0 ? k + 4 : k + 3;
     const int row_half = set == 0 ? 0 : LOADS / 2;
+    if constexpr (seg2) {
+      if (set == 0) {
+        pkb0 = npkb0;
+        pkb1 = npkb1;
+      } else {
+        npkb0 = kmap(k + 5);
+        npkb1 = kmap(k + 6);
+      }
+    }
 #pragma unroll
     for (int g = 0; g < LOADS; ++g) {
-      issue_load(pair0 + (g & 1), row_half + g / 2);
+      const int st = pair0 + (g & 1);
+      issue_load(st, seg2 ? ((g & 1) ? pkb1 : pkb0) : st, row_half + g / 2);
 #pragma unroll
       for (int r = 0; r < Cfg::NREADS; ++r)
         if (r * RGROUPS / Cfg::NREADS == g) read_one(rbase, r, set ^ 1);
@@ -484,9 +519,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
 
-  // With every column an outlier column the int8 codes are all zero and the
-  // int8 segment is skipped.
-  const int nk = (seg2 && n_o == K) ? 0 : (K + BK - 1) / BK;
   const std::integral_constant<bool, false> kInt8{};
   const std::integral_constant<bool, true> kF16{};
   // Runs main-loop steps 0 .. steps-1 over the current operands, after
@@ -494,6 +526,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // first wait leaves in flight the second pair and at most one load before
   // it (stage 1's last, or the last outlier gather), so stage 0 has landed.
   auto run_steps = [&](int steps, auto f16) __attribute__((always_inline)) {
+    if constexpr (seg2) {
+      npkb0 = kmap(4);
+      npkb1 = kmap(5);
+    }
     wait_vmcnt<2 * LOADS + 1>();
     lds_barrier();
     read_frags(0, 0);
@@ -716,6 +752,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       rstride = rowbytes = (int)(2 * ldo);
       rsrc = make_rsrc(seg_base, (uint32_t)op_rows_valid * (uint32_t)rowbytes);
       set_offsets();
+      list_on = false;   // the outlier columns, in order
       lds_barrier();   // every wave has read its factors
       issue_pair(0);
       issue_pair(2);
@@ -912,31 +949,34 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
                          int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                          const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                          const uint16_t* Wo, int wo_cols, const uint16_t* Wf, const uint16_t* Xd,
-                         const uint32_t* bmp, hipStream_t s) {
+                         const uint32_t* bmp, const int32_t* kbl, hipStream_t s) {
   const dim3 grid((unsigned)(((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN)));
   const dim3 block(Cfg::THREADS);
   if (C) {
     // parity mode: the epilogue outlier path only
     hipLaunchKernelGGL((k_gemm_i8<Cfg, kInt32>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M, (int)N,
-                       (int)K, Xo, cols, n_out, bias, Y, C, nullptr, 0, Wf, nullptr, nullptr);
+                       (int)K, Xo, cols, n_out, bias, Y, C, nullptr, 0, Wf, nullptr, nullptr,
+                       nullptr);
     return hipGetLastError();
   }
   // The outlier count is only known on the device: with a second segment
   // possible, its mode is launched too and the one whose case it is not
   // returns at once.
   hipLaunchKernelGGL((k_gemm_i8<Cfg, kPlain>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M, (int)N,
-                     (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
+                     (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp, nullptr);
   if (Wo) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemm_i8<Cfg, kOutlierSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
-                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
+                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp,
+                       kbl);
   }
   if (Xd && bmp) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemm_i8<Cfg, kDenseSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
-                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp);
+                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp,
+                       kbl);
   }
   return hipGetLastError();
 }
@@ -957,7 +997,8 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo, const int32_t* cols,
                        const int32_t* n_out, const uint16_t* bias, uint16_t* Y, int32_t* C,
                        const uint16_t* Wo, int wo_cols, const uint16_t* Wf,
-                       const uint16_t* Xd, const uint32_t* bmp, hipStream_t s) {
+                       const uint16_t* Xd, const uint32_t* bmp, const int32_t* kbl,
+                       hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   // (K == 0 goes to the tiled kernel, whose empty main loop leaves only the
   // epilogue: Y = bias, or 0)
@@ -968,9 +1009,9 @@ hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, cons
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_large >= kLargeTileMin)
     return launch_gemm_t<CfgLarge>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo,
-                                   wo_cols, Wf, Xd, bmp, s);
+                                   wo_cols, Wf, Xd, bmp, kbl, s);
   return launch_gemm_t<CfgSmall>(Xq, Wq, sx, sw, M, N, K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols,
-                                 Wf, Xd, bmp, s);
+                                 Wf, Xd, bmp, kbl, s);
 }
 
 }  // namespace i8mm

@@ -40,10 +40,13 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* 
                        hipStream_t s);
 // The same with the flags given as `bands` partial bitmaps (bands x
 // ceil(K/32) words, see launch_outlier_flag_bands); the first block also
-// writes their OR to bitmap_out when it is given.
+// writes their OR to bitmap_out when it is given, and, when kbl is given,
+// the list of 64-column k-blocks that hold a normal column (kbl[0] = count,
+// then the blocks ascending; 1 + ceil(K/64) ints).
 hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
                               int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
-                              uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s);
+                              uint16_t* Xo, int32_t* cols, int32_t* n_out, int32_t* kbl,
+                              hipStream_t s);
 
 // Wo: the fp16 outlier weight columns [N, LD(n)] written by
 // launch_recover_outlier_w (or launch_gather_w_cols) with room for wo_cols
@@ -54,12 +57,14 @@ hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uin
 // all K columns. Otherwise the outlier product runs in the epilogue. Wf: the
 // fp16 weight [N, K] when the layer keeps one (its columns are the outlier
 // weights), or nullptr (they are recovered from Wq and sw).
+// kbl: the k-block list of launch_rows_banded, or nullptr; given, the
+// int8 loop of the segment modes visits only those k-blocks.
 hipError_t launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* sx, const float* sw,
                        int64_t M, int64_t N, int64_t K, const uint16_t* Xo,
                        const int32_t* cols, const int32_t* n_out, const uint16_t* bias,
                        uint16_t* Y, int32_t* C, const uint16_t* Wo, int wo_cols,
                        const uint16_t* Wf, const uint16_t* Xd, const uint32_t* bmp,
-                       hipStream_t s);
+                       const int32_t* kbl, hipStream_t s);
 
 // Wo[j, t] = fp16(fl32(fl32(Wq[j, cols[t]] * sw[j]) / 127)) for t < n, +0.0 up
 // to LD(n); nothing when n <= 16 or n > wo_cols (n read on the device).

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
                                               uint32_t* __restrict__ bitmap_out,
                                               int8_t* __restrict__ Xq, float* __restrict__ sx,
                                               uint16_t* __restrict__ Xo, int32_t* __restrict__ cols,
-                                              int32_t* __restrict__ n_out) {
+                                              int32_t* __restrict__ n_out,
+                                              int32_t* __restrict__ kbl) {
   constexpr bool kFlags = FMODE != kNoFlags;
   extern __shared__ uint32_t smem[];
   __shared__ int sred[kRowThreads / kWave];
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
   if (blockIdx.x == 0) {
     if constexpr (kFlags) {
       write_cols(sbm, spre, nwords, n, cols, n_out);
+      write_kblocks(sbm, K, kbl);
       if (bitmap_out)
         for (int w = tid; w < nwords; w += kRowThreads) bitmap_out[w] = sbm[w];
     } else {
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ flags,
     int bands, uint32_t* __restrict__ bitmap_out, int8_t* __restrict__ Xq,
     float* __restrict__ sx, uint16_t* __restrict__ Xo, int32_t* __restrict__ cols,
-    int32_t* __restrict__ n_out) {
+    int32_t* __restrict__ n_out, int32_t* __restrict__ kbl) {
   static_assert(CPB > 0 && CPB <= 8 && FMODE != kNoFlags, "flagged rows, K <= 16384");
   extern __shared__ uint32_t smem[];
   __shared__ int sred[kRowThreads / kWave];
@@ -469,6 +471,7 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
   if (Xo || cols || n_out) n = bitmap_prefix<true>(sbm, spre, nwords, sred);
   if (blockIdx.x == 0) {
     write_cols(sbm, spre, nwords, n, cols, n_out);
+    write_kblocks(sbm, K, kbl);
     if (bitmap_out)
       for (int w = tid; w < nwords; w += kRowThreads) bitmap_out[w] = sbm[w];
   }
@@ -573,21 +576,22 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
 template <int CPB>
 hipError_t launch_rows_flagged_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
                                  int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
-                                 uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s) {
+                                 uint16_t* Xo, int32_t* cols, int32_t* n_out, int32_t* kbl,
+                                 hipStream_t s) {
   const int nwords = (int)((K + 31) / 32);
   const size_t shm = (size_t)nwords * 2 * sizeof(uint32_t);
   // four resident blocks per CU on 256 CUs; each block walks its rows
   const int64_t blocks = std::min<int64_t>(M, 1024);
   auto kern = bands == 1 ? k_rows_flagged<CPB, kBitmap> : k_rows_flagged<CPB, kBands>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K, flags,
-                     bands, bitmap_out, Xq, sx, Xo, cols, n_out);
+                     bands, bitmap_out, Xq, sx, Xo, cols, n_out, kbl);
   return hipGetLastError();
 }
 
 template <int CPT>
 hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
                          int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx, uint16_t* Xo,
-                         int32_t* cols, int32_t* n_out, hipStream_t s) {
+                         int32_t* cols, int32_t* n_out, int32_t* kbl, hipStream_t s) {
   const int nwords = (int)((K + 31) / 32);
   const size_t shm = flags ? (size_t)nwords * 2 * sizeof(uint32_t) : 0;
   // 4 rows per block (one per wavefront) while that keeps >= 1024 blocks;
@@ -598,7 +602,7 @@ hipError_t launch_rows_t(const uint16_t* X, int64_t M, int64_t K, const uint32_t
   auto kern = !flags ? k_rows<CPT, kNoFlags> : bands == 1 ? k_rows<CPT, kBitmap>
                                                            : k_rows<CPT, kBands>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K, (int)rpb,
-                     flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out);
+                     flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, kbl);
   return hipGetLastError();
 }
 
@@ -813,13 +817,14 @@ hipError_t launch_cols_from_bitmap(const uint32_t* bitmap, int64_t K, int32_t* c
 
 hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uint32_t* flags,
                               int bands, uint32_t* bitmap_out, int8_t* Xq, float* sx,
-                              uint16_t* Xo, int32_t* cols, int32_t* n_out, hipStream_t s) {
+                              uint16_t* Xo, int32_t* cols, int32_t* n_out, int32_t* kbl,
+                              hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (flags && K > 0) {
     // the block-per-row pass (chunks per thread: ceil(K / 2048))
     const int64_t cpb = (K / 8 + kRowThreads - 1) / kRowThreads;
 #define I8MM_ROWSF(CPB) \
-  launch_rows_flagged_t<CPB>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, s)
+  launch_rows_flagged_t<CPB>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, kbl, s)
     if (cpb <= 1) return I8MM_ROWSF(1);
     if (cpb <= 2) return I8MM_ROWSF(2);
     if (cpb <= 4) return I8MM_ROWSF(4);
@@ -829,7 +834,7 @@ hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uin
   }
   const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
 #define I8MM_ROWS(CPT) \
-  launch_rows_t<CPT>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, s)
+  launch_rows_t<CPT>(X, M, K, flags, bands, bitmap_out, Xq, sx, Xo, cols, n_out, kbl, s)
   if (per_lane <= 1) return I8MM_ROWS(1);
   if (per_lane <= 2) return I8MM_ROWS(2);
   if (per_lane <= 4) return I8MM_ROWS(4);
@@ -844,7 +849,7 @@ hipError_t launch_rows_banded(const uint16_t* X, int64_t M, int64_t K, const uin
 hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const uint32_t* bitmap,
                        int8_t* Xq, float* sx, uint16_t* Xo, int32_t* cols, int32_t* n_out,
                        hipStream_t s) {
-  return launch_rows_banded(X, M, K, bitmap, 1, nullptr, Xq, sx, Xo, cols, n_out, s);
+  return launch_rows_banded(X, M, K, bitmap, 1, nullptr, Xq, sx, Xo, cols, n_out, nullptr, s);
 }
 
 int flag_bands(int64_t M, int64_t K) {

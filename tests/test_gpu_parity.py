@@ -284,7 +284,8 @@ def test_linear_edge_cases(gpu, case):
 
 
 @pytest.mark.parametrize("case", ["n17", "n33", "n70", "n100", "all_columns", "large_tiles_n40",
-                                  "large_tiles_all", "wide_all", "n600"])
+                                  "large_tiles_all", "wide_all", "n600", "block_run",
+                                  "tail_block"])
 def test_linear_many_outliers(gpu, case):
     """More than 16 outlier columns, three workspaces: the minimal one, the
     default region of recovered weights (workspace_bytes(M, K, N), room for
@@ -296,7 +297,11 @@ def test_linear_many_outliers(gpu, case):
     in the epilogue. Without room the GEMM's dense second loop runs over all
     K columns (all columns outliers: the int8 loop is skipped). Every Y within
     the tolerance of the oracle. wide_all: N * LD(K) / 8 = 1.07M 16-byte
-    pieces, more than one pass of the recovery's grid."""
+    pieces, more than one pass of the recovery's grid. block_run and
+    tail_block make whole 64-column k-blocks outlier columns (ten in a row;
+    the partial last block), which the int8 loop of the segment modes skips:
+    their codes are all zero, so the int32 sums, and Y against the step
+    call, stay bit for bit."""
     note("linear many outliers %s" % case)
     rng = np.random.default_rng(300 + len(case))
     large = case.startswith("large_tiles")
@@ -307,6 +312,11 @@ def test_linear_many_outliers(gpu, case):
     tau = 6.0
     if case.endswith("all") or case == "all_columns":
         tau = 0.0
+    elif case in ("block_run", "tail_block"):
+        run = list(range(64, 704)) if case == "block_run" else list(range(100, 140)) + \
+            list(range(1024, 1040))
+        rows = rng.integers(0, M, size=len(run))
+        X[rows, run] = np.where(rng.random(len(run)) < 0.5, -7.5, 7.5).astype(np.float16)
     else:
         n_plant = int(case.split("n")[-1])
         synth.plant_outlier_columns(rng, X, n_plant, 7.0, 30.0, (0.05, 0.6))
