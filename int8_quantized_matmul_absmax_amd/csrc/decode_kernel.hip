@@ -21,21 +21,29 @@
 //                    (CB * SCB / 127) or fp16 weight columns ([HF-blog]
 //                    "Usage"; [Summary] steps 3-4).
 //
-// Block = 4 wavefronts. Every block does the X side itself (X is at most
-// 8 x 16384 fp16, read from L2 by all blocks). Thread t holds the 16-byte
-// chunks t, t + 256, ... of every token row in registers, so each 8-column
-// flag mask is its own maximum over the rows (no exchange beyond the four
-// lanes of a bitmap word), the outlier elements are masked out from its own
-// bits, and the row maxima need one block reduction for all rows at once.
-// The X loads are issued before the first weight tile's loads and waited for
-// alone, so the X side runs while the weight is in flight. The codes go to
-// LDS; block 0 also writes the intermediates (bitmap, cols, n, sx, Xq, Xo)
-// to the workspace. Then blocks walk 16-feature weight tiles (persistent
-// grid) like the few-token GEMV: waves split K in 256-byte chunks, weight
-// rows straight from HBM into registers in the operand layout of
-// v_mfma_i32_16x16x64_i8, token fragments from the LDS codes (rows padded so
-// the 16 token rows of one read hit distinct banks), partial tiles summed
-// through LDS.
+// Block = 8 wavefronts in two roles. Waves 0-3 stream the block's 16-feature
+// weight tiles straight from HBM into registers (in the operand layout of
+// v_mfma_i32_16x16x64_i8: waves split K in 256-byte chunks) and run the
+// MFMAs. Waves 4-7 do the X side and the epilogue. Every block does the X
+// side itself (X is at most 8 x 16384 fp16 and comes from L2): a weight
+// wave is held up issuing its loads until the memory system takes them,
+// about as long as the weight takes to stream, so an X side that shared its
+// waves started only when the weight had almost landed. Split, it runs while
+// the weight streams. The X waves' loads go out first (a barrier orders them
+// before the weight loads); all barriers are LDS-only, so none waits for
+// loads in flight.
+//
+// X side: X-wave thread t holds the 16-byte chunks t, t + 256, ... of every
+// token row in registers, so each 8-column flag mask is its own maximum over
+// the rows, the outlier elements are masked out from its own bits, and the
+// row maxima and outlier counts need one exchange between the four X waves
+// (after a barrier every X thread knows the row scales and its chunks'
+// positions in the ascending outlier column list). The codes go to LDS;
+// block 0 also writes the intermediates (bitmap, cols, n, sx, Xq, Xo) to the
+// workspace. Then, per tile, the X waves gather the tile's outlier weights
+// while the weight waves run the MFMAs (token fragments from the LDS codes,
+// rows padded so the 16 token rows of one read hit distinct banks), the
+// partial tiles meet in LDS, and the X waves write Y.
 
 #include <atomic>
 #include <algorithm>
@@ -47,14 +55,15 @@ namespace i8mm {
 
 namespace {
 
-constexpr int kDcThreads = kBlockThreads;   // 4 wavefronts
-constexpr int kDcWaves = kDcThreads / kWave;
+constexpr int kDcThreads = 512;             // 8 wavefronts
+constexpr int kDcWWaves = 4;                // waves 0-3: weight tiles and MFMAs
+constexpr int kDcXThreads = 256;            // waves 4-7: X side and epilogue
 constexpr int kDcFeat = 16;                 // output features per tile
 constexpr int kDcChunk = 256;               // K bytes per MFMA chunk
 constexpr int kDcBatch = 4;                 // chunks per wave held in registers at once
 constexpr int kDcMaxTok = 8;
 constexpr int kDcMaxOut = 32;               // outlier columns staged in LDS
-constexpr int kDcXRegs = 32;                // 16-byte X chunks a thread holds
+constexpr int kDcXRegs = 32;                // 16-byte X chunks an X thread holds
 constexpr int kDcPad = 16;                  // LDS row padding of the codes
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dc_rsrc(const void* base, uint32_t bytes) {
@@ -72,12 +81,12 @@ __host__ __device__ constexpr int dc_round16(int v) { return (v + 15) / 16 * 16;
 // the 16 token rows of one fragment read hit distinct banks.
 __host__ __device__ constexpr int dc_pitch(int K) { return (K + 255) / 256 * 256 + kDcPad; }
 
-// Dynamic LDS: [codes M x pitch][bitmap][prefix].
+// Dynamic LDS: [codes M x pitch][bitmap].
 __host__ __device__ constexpr int dc_lds_bytes(int M, int K) {
-  return dc_round16(M * dc_pitch(K)) + 8 * ((K + 31) / 32);
+  return dc_round16(M * dc_pitch(K)) + 4 * ((K + 31) / 32);
 }
 
-// Thread t holds the 16-byte chunks t, t + 256, ... (JC of them, K <= JC *
+// X thread t holds the 16-byte chunks t, t + 256, ... (JC of them, K <= JC *
 // 2048) of each of the first MR token rows (M <= MR, MR * JC <= kDcXRegs).
 template <int MR, int JC>
 __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
@@ -86,73 +95,143 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wf, uint32_t* __restrict__ bitmap_g,
     int32_t* __restrict__ cols_g, int32_t* __restrict__ n_g, float* __restrict__ sx_g,
     int8_t* __restrict__ Xq_g, uint16_t* __restrict__ Xo_g) {
-  static_assert(MR * JC <= kDcXRegs, "X chunks held per thread");
+  static_assert(MR * JC <= kDcXRegs && MR <= kDcMaxTok, "X chunks held per thread");
+  constexpr int XW = kDcXThreads / kWave;   // X waves
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-  __shared__ int32_t red[kDcWaves][16 * 16];
+  __shared__ int32_t red[kDcWWaves][16 * 16];
   __shared__ float s_wo[kDcMaxOut][16];             // outlier weights, [t][j]
   __shared__ uint16_t s_xo[kDcMaxTok][kDcMaxOut];   // outlier activations, [m][t]
   __shared__ float s_sx[kDcMaxTok];
   __shared__ int s_cols[kDcMaxOut];
-  __shared__ int sred[kDcWaves];
-  __shared__ uint32_t s_rmax[kDcWaves][kDcMaxTok];   // per-wave row maxima
+  __shared__ int s_cnt[XW][JC];                     // outlier columns per X wave and j
+  __shared__ uint32_t s_rmax[XW][kDcMaxTok];        // row maxima per X wave
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nchunks = K / 8;            // 16-byte chunks of a row
+  const bool wrole = wave < kDcWWaves;      // uniform per wave
+  const int xt = tid - kDcXThreads;         // X-side thread index (X waves)
+  const int xw = wave - kDcWWaves;          // X wave index (X waves)
+  const int nchunks = K / 8;                // 16-byte chunks of a row
   const int nwords = (K + 31) / 32;
-  const int ldx = dc_pitch(K);          // LDS row pitch of the codes (bytes)
+  const int ldx = dc_pitch(K);              // LDS row pitch of the codes (bytes)
   int8_t* s_xq = reinterpret_cast<int8_t*>(dsm);
   uint32_t* sbm = reinterpret_cast<uint32_t*>(dsm + dc_round16(M * ldx));
-  uint32_t* spre = sbm + nwords;
   const bool first = blockIdx.x == 0;
+  const int jf = xt & 15, mt = xt >> 4;     // epilogue (X waves): feature jf, token mt
 
-  // ---- X into registers (issued first: waited for alone below)
+  const int nkc = (K + kDcChunk - 1) / kDcChunk;
+  const int r16 = lane & 15;                 // weight row / token of the MFMA operands
+  const int seg = (lane >> 4) * 16;          // this lane's 16 bytes of each 64-byte k-slice
+
+  // The two roles run separate code between the same sequence of barriers:
+  // B0 (the X loads are out), B1 (the X waves' flag words, counts and row
+  // maxima), B2 (codes, row factors and staged outlier columns), then two
+  // per tile (partial tiles and outlier weights in LDS; LDS free again).
+  if (wrole) {
+    // ---- weight waves
+    constexpr int kOob = 0x7ffffff0;
+    v4i32 wf[kDcBatch][4];
+    __amdgpu_buffer_rsrc_t rw;
+    auto load_w = [&](int c0) {
+#pragma unroll
+      for (int b = 0; b < kDcBatch; ++b) {
+        const int c = c0 + b * kDcWWaves;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = c * kDcChunk + 64 * j + seg;
+          wf[b][j] = __builtin_bit_cast(
+              v4i32, __builtin_amdgcn_raw_buffer_load_b128(
+                         rw, (c < nkc && k < K) ? r16 * K + k : kOob, 0, 0));
+        }
+      }
+    };
+    auto tile_rsrc = [&](int64_t f0) {
+      const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
+      rw = dc_rsrc(Wq + f0 * K, (uint32_t)rows_w * (uint32_t)K);
+    };
+    lds_only_barrier();   // B0
+    tile_rsrc((int64_t)blockIdx.x * kDcFeat);
+    load_w(wave);
+    lds_only_barrier();   // B1
+    lds_only_barrier();   // B2
+    for (int64_t tile = blockIdx.x; tile * kDcFeat < N; tile += gridDim.x) {
+      v4i32 acc = v4i32{0, 0, 0, 0};
+      const int8_t* xrow = s_xq + (r16 < M ? r16 : 0) * ldx;
+      for (int c0 = wave; c0 < nkc; c0 += kDcWWaves * kDcBatch) {
+        if (c0 != wave) load_w(c0);
+        v4i32 xf[kDcBatch][4];
+#pragma unroll
+        for (int b = 0; b < kDcBatch; ++b) {
+          const int c = c0 + b * kDcWWaves;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k = c * kDcChunk + 64 * j + seg;
+            const bool ok = r16 < M && c < nkc && k < K;
+            const v4i32 v = *reinterpret_cast<const v4i32*>(xrow + (ok ? k : 0));
+            xf[b][j] = ok ? v : v4i32{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kDcBatch; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[b][j], xf[b][j], acc, 0, 0, 0);
+      }
+      // D layout of the 16x16 MFMA: lane l, register r -> token l%16 (B
+      // column), feature 4*(l/16) + r (A row).
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(4 * (lane >> 4) + r) * 16 + r16] = acc[r];
+      // the next tile's weight is in flight during this tile's epilogue
+      const int64_t next = tile + gridDim.x;
+      if (next * kDcFeat < N) {
+        tile_rsrc(next * kDcFeat);
+        load_w(wave);
+      }
+      lds_only_barrier();   // partial tiles in LDS
+      lds_only_barrier();   // the epilogue has read them
+    }
+    return;
+  }
+
+  // ---- X waves: X into registers, then the first tile's factors
   uint4 xr[MR][JC];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
 #pragma unroll
     for (int j = 0; j < JC; ++j) {
-      const int c = tid + kDcThreads * j;
+      const int c = xt + kDcXThreads * j;
       xr[m][j] = (m < M && c < nchunks) ? ld16(X + (int64_t)m * K + c * 8) : make_uint4(0, 0, 0, 0);
     }
   }
-
-  // ---- the first weight tile's loads
-  const int nkc = (K + kDcChunk - 1) / kDcChunk;
-  const int r16 = lane & 15;                 // weight row / token of the MFMA operands
-  const int seg = (lane >> 4) * 16;          // this lane's 16 bytes of each 64-byte k-slice
-  constexpr int kOob = 0x7ffffff0;
-  v4i32 wf[kDcBatch][4];
-  __amdgpu_buffer_rsrc_t rw;
-  auto load_w = [&](int c0) {
-#pragma unroll
-    for (int b = 0; b < kDcBatch; ++b) {
-      const int c = c0 + b * kDcWaves;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = c * kDcChunk + 64 * j + seg;
-        wf[b][j] = __builtin_bit_cast(
-            v4i32, __builtin_amdgcn_raw_buffer_load_b128(
-                       rw, (c < nkc && k < K) ? r16 * K + k : kOob, 0, 0));
-      }
-    }
+  float sw_f = 0.0f, bias_f = 0.0f;
+  auto load_factors = [&](int64_t f0) {
+    const int64_t f = f0 + jf;
+    sw_f = f < N ? sw[f] : 0.0f;
+    bias_f = (bias && f < N) ? h2f(bias[f]) : 0.0f;
   };
-  auto tile_rsrc = [&](int64_t f0) {
-    const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
-    rw = dc_rsrc(Wq + f0 * K, (uint32_t)rows_w * (uint32_t)K);
-  };
-  tile_rsrc((int64_t)blockIdx.x * kDcFeat);
-  load_w(wave);
-  __builtin_amdgcn_sched_barrier(0);
+  load_factors((int64_t)blockIdx.x * kDcFeat);
+  lds_only_barrier();   // B0
 
-  // ---- column flags: a thread holds whole columns, so each 8-column mask
-  // is its own maximum over the rows; the four masks of a 32-column word are
-  // OR-ed by shuffles (consecutive threads hold consecutive chunks)
+  // column flags (a thread holds whole columns, so each 8-column mask is its
+  // own maximum over the rows; the four masks of a 32-column word are OR-ed
+  // by shuffles), each thread's place in the ascending outlier list within
+  // its wave, and the row maxima over the normal columns (outlier elements
+  // masked out from the thread's own bits)
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  auto strip = [&](uint32_t bits, const uint4& t) -> uint4 {
+    uint32_t h[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t b = bits >> (2 * q);
+      h[q] &= ((b & 1u) ? 0u : 0x0000ffffu) | ((b & 2u) ? 0u : 0xffff0000u);
+    }
+    return make_uint4(h[0], h[1], h[2], h[3]);
+  };
   uint32_t om[JC];   // outlier bits of chunk j (bit e: element e)
+  int excl[JC];      // outlier columns before chunk j's within the wave
 #pragma unroll
   for (int j = 0; j < JC; ++j) {
-    const int c = tid + kDcThreads * j;
+    const int c = xt + kDcXThreads * j;
     u16x2 mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx[i] = u16x2{0, 0};
@@ -175,43 +254,15 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     uint32_t word = om[j] << (8 * (c & 3));
     word |= (uint32_t)__shfl_xor((int)word, 1, kWave);
     word |= (uint32_t)__shfl_xor((int)word, 2, kWave);
-    if ((c & 3) == 0 && c < nchunks) sbm[c >> 2] = word;
-  }
-  __syncthreads();
-  const int n = bitmap_prefix(sbm, spre, nwords, sred);
-  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
-#pragma unroll 1
-  for (int w = tid; w < nwords; w += kDcThreads) {
-    uint32_t bits = sbm[w];
-    int p = (int)spre[w];
-    while (bits && p < kDcMaxOut) {
-      s_cols[p++] = w * 32 + __builtin_ctz(bits);
-      bits &= bits - 1;
+    if ((c & 3) == 0 && c < nchunks) {
+      sbm[c >> 2] = word;
+      if (first) bitmap_g[c >> 2] = word;
     }
+    const int cnt = __popc(om[j]);
+    const int incl = wave_inclusive_scan(cnt, lane);
+    excl[j] = incl - cnt;
+    if (lane == kWave - 1) s_cnt[xw][j] = incl;
   }
-  if (first) {
-#pragma unroll 1
-    for (int w = tid; w < nwords; w += kDcThreads) bitmap_g[w] = sbm[w];
-    write_cols(sbm, spre, nwords, n, cols_g, n_g);
-#pragma unroll 1
-    for (int64_t i = tid; i < (int64_t)M * (ld - n); i += kDcThreads) {
-      const int64_t m = i / (ld - n);
-      Xo_g[m * ld + n + (i - m * (ld - n))] = 0;
-    }
-  }
-
-  // ---- row absmax over the block, outlier elements masked out (branch-free,
-  // from the thread's own flag bits): per thread, per wave (DPP), then the
-  // four waves through LDS
-  auto strip = [&](uint32_t bits, const uint4& t) -> uint4 {
-    uint32_t h[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t b = bits >> (2 * q);
-      h[q] &= ((b & 1u) ? 0u : 0x0000ffffu) | ((b & 2u) ? 0u : 0xffff0000u);
-    }
-    return make_uint4(h[0], h[1], h[2], h[3]);
-  };
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m < M) {
@@ -224,134 +275,111 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
         for (int i = 0; i < 4; ++i)
           m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
       }
-      const uint32_t mx = wave_max_u32_dpp(m2[0] > m2[1] ? m2[0] : m2[1]);
-      if (lane == 0) s_rmax[wave][m] = mx;
+      const uint32_t mxw = wave_max_u32_dpp(m2[0] > m2[1] ? m2[0] : m2[1]);
+      if (lane == 0) s_rmax[xw][m] = mxw;
     }
   }
-  __syncthreads();
+  lds_only_barrier();   // B1
 
-  // ---- codes into LDS (block 0: also the workspace)
+  // positions (chunk order: j, then X wave, then lane), codes, outlier
+  // columns and activations
+  int pos0[JC];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < JC; ++j) {
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < XW; ++w) {
+      const int v = s_cnt[w][j];
+      before += w < xw ? v : 0;
+      tot += v;
+    }
+    pos0[j] = n + before + excl[j];
+    n += tot;
+  }
+  const int64_t ld = ((int64_t)n + 31) / 32 * 32;
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m < M) {
       uint32_t mx = s_rmax[0][m];
 #pragma unroll
-      for (int w = 1; w < kDcWaves; ++w) mx = mx > s_rmax[w][m] ? mx : s_rmax[w][m];
+      for (int w = 1; w < XW; ++w) mx = mx > s_rmax[w][m] ? mx : s_rmax[w][m];
       const float a = h2f(mx);
-      const float s = a != 0.0f ? 127.0f / a : 0.0f;
+      const float sc = a != 0.0f ? 127.0f / a : 0.0f;
 #pragma unroll
       for (int j = 0; j < JC; ++j) {
-        const int c = tid + kDcThreads * j;
+        const int c = xt + kDcXThreads * j;
         if (c < nchunks) {
-          const uint2 q = codes8_rne(strip(om[j], xr[m][j]), s);
+          const uint2 q = codes8_rne(strip(om[j], xr[m][j]), sc);
           *reinterpret_cast<uint2*>(s_xq + m * ldx + c * 8) = q;
           if (first) *reinterpret_cast<uint2*>(Xq_g + (int64_t)m * K + c * 8) = q;
         }
       }
-      if (tid == 0) {
+      if (xt == 0) {
         s_sx[m] = a;
         if (first) sx_g[m] = a;
       }
     }
   }
-
-  // ---- outlier activations (a chunk with a set bit; rare), last: its loop
-  // may wait for the weight loads, which the tiles wait for anyway
 #pragma unroll
   for (int j = 0; j < JC; ++j) {
-    if (om[j]) {
-      const int c = tid + kDcThreads * j;
-      const int w = c >> 2, sh = 8 * (c & 3);
-      const int pos0 = (int)spre[w] + __popc(sbm[w] & ((1u << sh) - 1u));
-#pragma unroll 1
-      for (int e = 0; e < 8; ++e) {
+    if (om[j]) {   // (rare)
+      const int c = xt + kDcXThreads * j;
+      int pos = pos0[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {   // (unrolled: e indexes the registers of X)
         if ((om[j] >> e) & 1u) {
-          const int pos = pos0 + __popc(om[j] & ((1u << e) - 1u));
+          const int col = c * 8 + e;
+          if (pos < kDcMaxOut) s_cols[pos] = col;
+          if (first) cols_g[pos] = col;
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
             if (m < M) {
-              // select from a copy: no dynamic index into the register array
-              const uint4 t = xr[m][j];
-              const uint32_t wd = (e >> 1) == 0 ? t.x : (e >> 1) == 1 ? t.y : (e >> 1) == 2 ? t.z : t.w;
-              const uint16_t v = (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu));
+              const uint16_t v = (uint16_t)half_of(xr[m][j], e);
               if (pos < kDcMaxOut) s_xo[m][pos] = v;
               if (first) Xo_g[m * ld + pos] = v;
             }
           }
+          ++pos;
         }
       }
     }
   }
-  __syncthreads();
+  if (first) {
+    if (xt == 0) *n_g = n;
+#pragma unroll 1
+    for (int64_t i = xt; i < (int64_t)M * (ld - n); i += kDcXThreads) {
+      const int64_t m = i / (ld - n);
+      Xo_g[m * ld + n + (i - m * (ld - n))] = 0;
+    }
+  }
+  lds_only_barrier();   // B2
 
-  // ---- weight tiles
+  // per tile: the tile's outlier weights while the weight waves run the
+  // MFMAs, then Y
   const bool staged = n <= kDcMaxOut;
-  const int jf = tid & 15, mt = tid >> 4;   // epilogue: feature jf, token mt
   bool first_tile = true;
   for (int64_t tile = blockIdx.x; tile * kDcFeat < N; tile += gridDim.x) {
     const int64_t f0 = tile * kDcFeat;
     const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
-    if (!first_tile) {
-      tile_rsrc(f0);
-      load_w(wave);
-    }
+    if (!first_tile) load_factors(f0);
     first_tile = false;
-    const int64_t f = f0 + jf;
-    const bool f_ok = jf < rows_w;
-    const float sw_f = f_ok ? sw[f] : 0.0f;
-    const float bias_f = (bias && f_ok) ? h2f(bias[f]) : 0.0f;
-    int qv[2] = {0, 0};
     if (staged && n > 0) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int t = (tid >> 4) + 16 * s2, j = tid & 15;
-        if (t < n && j < rows_w) {
-          const int64_t off = (f0 + j) * K + s_cols[t];
-          qv[s2] = Wf ? (int)Wf[off] : (int)Wq[off];
+        const int t = mt + 16 * s2;
+        if (t < n && jf < rows_w) {
+          const int64_t off = (f0 + jf) * K + s_cols[t];
+          s_wo[t][jf] = Wf ? h2f(Wf[off]) : h2f(f2h(((float)Wq[off] * sw_f) / 127.0f));
         }
       }
     }
-
-    v4i32 acc = v4i32{0, 0, 0, 0};
-    const int8_t* xrow = s_xq + (r16 < M ? r16 : 0) * ldx;
-    for (int c0 = wave; c0 < nkc; c0 += kDcWaves * kDcBatch) {
-      if (c0 != wave) load_w(c0);
-      v4i32 xf[kDcBatch][4];
-#pragma unroll
-      for (int b = 0; b < kDcBatch; ++b) {
-        const int c = c0 + b * kDcWaves;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int k = c * kDcChunk + 64 * j + seg;
-          const bool ok = r16 < M && c < nkc && k < K;
-          const v4i32 v = *reinterpret_cast<const v4i32*>(xrow + (ok ? k : 0));
-          xf[b][j] = ok ? v : v4i32{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kDcBatch; ++b)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[b][j], xf[b][j], acc, 0, 0, 0);
-    }
-    // D layout of the 16x16 MFMA: lane l, register r -> token l%16 (B
-    // column), feature 4*(l/16) + r (A row).
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][(4 * (lane >> 4) + r) * 16 + r16] = acc[r];
-    if (staged && n > 0) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int t = (tid >> 4) + 16 * s2, j = tid & 15;
-        if (t < n && j < rows_w)
-          s_wo[t][j] = Wf ? h2f((uint32_t)qv[s2]) : h2f(f2h(((float)qv[s2] * sw[f0 + j]) / 127.0f));
-      }
-    }
-    __syncthreads();
-
-    if (f_ok && mt < M) {
+    lds_only_barrier();   // partial tiles and outlier weights in LDS
+    if (jf < rows_w && mt < M) {
+      const int64_t f = f0 + jf;
       int32_t acc_s = 0;
 #pragma unroll
-      for (int w = 0; w < kDcWaves; ++w) acc_s += red[w][jf * 16 + mt];
+      for (int w = 0; w < kDcWWaves; ++w) acc_s += red[w][jf * 16 + mt];
       const float fw = sw_f / 127.0f;
       const float y = (float)acc_s * (s_sx[mt] / 127.0f) * fw;
       float yo = 0.0f;
@@ -372,7 +400,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       }
       Y[(int64_t)mt * N + f] = f2h(y + yo + bias_f);
     }
-    __syncthreads();   // red and s_wo are rewritten by the next tile
+    lds_only_barrier();   // the next tile rewrites red and s_wo
   }
 }
 
@@ -397,7 +425,7 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
   if (!lds_set[slot].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_i8<MR, JC>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            dc_lds_bytes(MR, JC * kDcThreads * 8));
+                            dc_lds_bytes(MR, JC * kDcXThreads * 8));
     if (e != hipSuccess) return e;
     lds_set[slot].store(true, std::memory_order_release);
   }
@@ -408,24 +436,25 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
       cus = 256;
     g_cus[slot].store(cus, std::memory_order_release);
   }
-  // two blocks per CU while both fit in LDS (static part about 7.5 KiB)
-  const int64_t per_cu = lds + 8 * 1024 <= 80 * 1024 ? 2 : 1;
+  // one block of eight waves per CU (two waves per SIMD); blocks beyond the
+  // first round take further tiles in turn
   const int64_t tiles = (N + kDcFeat - 1) / kDcFeat;
-  const int64_t blocks = std::min<int64_t>(tiles, per_cu * cus);
-  hipLaunchKernelGGL((k_decode_i8<MR, JC>), dim3((unsigned)blocks), dim3(kDcThreads), (size_t)lds, s, X,
-                     Wq, sw, (int)M, (int)N, (int)K, tau16, bias, Y, Wf, bitmap, cols, n_out, sx,
-                     Xq, Xo);
+  const int64_t blocks = std::min<int64_t>(tiles, cus);
+  hipLaunchKernelGGL((k_decode_i8<MR, JC>), dim3((unsigned)blocks), dim3(kDcThreads), (size_t)lds,
+                     s, X, Wq, sw, (int)M, (int)N, (int)K, tau16, bias, Y, Wf, bitmap, cols,
+                     n_out, sx, Xq, Xo);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool decode_applies(int64_t M, int64_t K) {
-  // a thread holds ceil(K / 2048) chunks of each of MR rows, MR * chunks <=
-  // kDcXRegs: K <= 16384 for M <= 4, 8192 for M <= 8. Beyond 8 tokens the X
-  // side, repeated by every block, costs more than the launches it saves.
+  // an X thread holds ceil(K / 2048) chunks of each of MR rows, MR * chunks
+  // <= kDcXRegs: K <= 16384 for M <= 4, 8192 for M <= 8. Beyond 8 tokens the
+  // X side, repeated by every block, outlasts the weight stream (16 tokens
+  // at 4096 -> 4096: 22 us in one launch against 15 us as separate kernels).
   if (M < 1 || M > kDcMaxTok || K < 16) return false;
-  const int64_t jc = (K + kDcThreads * 8 - 1) / (kDcThreads * 8);
+  const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
   return jc <= (M <= 4 ? 8 : 4);
 }
 
@@ -434,7 +463,8 @@ hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, i
                          const uint16_t* Wf, uint32_t* bitmap, int32_t* cols, int32_t* n_out,
                          float* sx, int8_t* Xq, uint16_t* Xo, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const int64_t jc = (K + kDcThreads * 8 - 1) / (kDcThreads * 8);   // chunks per row per thread
+  // chunks per row per X thread
+  const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
 #define I8MM_DECODE(MR_, JC_)                                                                   \
   return launch_decode_t<MR_, JC_>(X, Wq, sw, M, N, K, tau16, bias, Y, Wf, bitmap, cols, n_out, \
                                    sx, Xq, Xo, s)

@@ -1,6 +1,6 @@
 """The single-launch few-token layer: the layer calls take it for M <= 8
-tokens with K <= 16384 (M <= 4) or 8192 (M <= 8), the columns of X a thread
-holds in registers; other few-token shapes (up to 64 tokens) take the
+tokens with K <= 16384 (M <= 4) or 8192 (M <= 8), the columns of X an X-side
+thread holds in registers; other few-token shapes (up to 64 tokens) take the
 separate kernels (also here).
 
 Against the oracle: every intermediate it writes to the workspace bit for
@@ -42,6 +42,9 @@ CASES = {
     "m16_fp16w_separate": (16, 4096, 300, 8, True, True),
     "m2_fp16w_n33": (2, 4112, 333, 33, False, True),
     "m20_fp16w_separate": (20, 4096, 300, 8, True, True),
+    "m24_k4096_separate": (24, 4096, 520, 6, True, False),
+    "m13_k4096_n40_separate": (13, 4096, 1000, 40, False, False),
+    "m1_k16384": (1, 16384, 700, 9, True, False),
 }
 
 
