@@ -61,6 +61,7 @@ def test_kernel_families_of_trace_names():
     assert bench._family(gemm % 0) == "k_gemm_i8"
     assert bench._family(gemm % 1) == "k_gemm_i8"
     assert bench._family(gemm % 2) == "k_gemm_i8_outlier_seg"
+    assert bench._family(gemm % 3) == "k_gemm_i8_dense_seg"
     assert bench._family("void i8mm::(anonymous namespace)::k_rows<2, true>(unsigned short "
                          "const*, long)") == "k_rows"
     assert bench._family("void at::native::elementwise_kernel<128, 4, at::native::copy_"
