@@ -545,26 +545,33 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     wait_vmcnt<0>();
   };
   // Dense outlier segment: the outlier product over all K columns, 32 columns
-  // per stage, three stage buffers, one barrier per stage, in the main loop's
-  // LDS layout (weight rows, then token rows, 64 bytes each, same swizzle),
-  // so the fragment reads and fp16 MFMAs are those of the compact segment.
-  // The weight tile comes through registers: thread t converts 16 columns of
+  // per stage through the five stage buffers, in the main loop's LDS layout
+  // (weight rows, then token rows, 64 bytes each, same swizzle), so the
+  // fragment reads and fp16 MFMAs are those of the compact segment. The
+  // weight tile comes through registers: thread t converts 16 columns of
   // weight row t / 2 exactly to fp16 (the int8 codes, or the fp16 weight Wf
   // itself) with the normal columns zeroed (bitmap word of the stage), and
   // writes them to LDS. The token rows are X itself, by DMA: X is finite on
   // the normal columns (a column holding inf or NaN is an outlier column),
   // so the zeroed weights remove them exactly. A stage whose bitmap word is 0
-  // issues no MFMA.
+  // issues no fragment reads and no MFMA.
+  // Step st: stage st+1's loads have landed; its weights go to LDS; barrier
+  // (stage st+1 visible to every wave; every wave is done reading stage st);
+  // the loads of stage st+4 (registers: set (st+4) % 4; DMA: the buffer of
+  // stage st-1); the fragment reads of stage st+1 into one register set and
+  // the MFMAs of stage st from the other. Loads past the last stage read
+  // zeros, so every step issues the same loads and the waits are fixed.
   auto dense_segment = [&]() __attribute__((always_inline)) {
-    constexpr int DNB = 3;
+    constexpr int DNB = STAGES;                 // stage buffers
     constexpr int DLB = BM / 16 / Cfg::WAVES;   // token-row DMA loads per wave and stage
     static_assert(Cfg::THREADS == 2 * BN, "two threads per weight row");
     static_assert(DLB * 16 * Cfg::WAVES == BM && DLB == 2, "token rows per wave");
-    static_assert(DNB * Cfg::STAGE_BYTES + 4 * ((I8MM_MAX_K + 31) / 32) <= Cfg::LDS_BYTES,
-                  "stages and the bitmap copy fit");
+    static_assert(DNB == 5, "four stages in flight");
     const int S = (K + 31) / 32;
-    uint32_t* s_dbm = reinterpret_cast<uint32_t*>(stages + DNB * Cfg::STAGE_BYTES);
-    for (int w = tid; w < S; w += Cfg::THREADS) s_dbm[w] = bmp[w];
+    // bitmap word of stage st (0 past the last stage): a scalar load
+    auto word_of = [&](int st) -> uint32_t {
+      return st < S ? __builtin_amdgcn_readfirstlane(bmp[st]) : 0u;
+    };
     // weight side: row ra, columns 16 * hf .. of each stage
     const int ra = tid >> 1, hf = tid & 1;
     const int rows_a = (int)min<int64_t>(BN, N - n0);
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
         ? make_rsrc(Wf + n0 * K, (uint32_t)rows_a * (uint32_t)K * 2u)
         : make_rsrc(Wq + n0 * K, (uint32_t)rows_a * (uint32_t)K);
     const int key_a = swz_key(ra);
-    uint4 areg[2][2];
+    uint4 areg[4][2];
     auto load_a = [&](int st, int set) {
       const int col = st * 32 + 16 * hf;
       const bool ok = col < K;
@@ -584,6 +591,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       } else {
         const int off = ok ? ra * K + col : 0x7ffffff0;
         areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+        // (unused here; a constant, so that the register sets of the two
+        // weight sources never merge with a register a load is still
+        // filling, which would make the compiler wait for every load)
+        areg[set][1] = make_uint4(0, 0, 0, 0);
       }
     };
     // token side: wave w fills token rows w * 32 + 16 p + lane / 4
@@ -609,6 +620,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + p * 16 * BK), 16, vo,
                                                  soff, 0, 0);
       }
+    };
+    // A 16-byte LDS store of the converted weights. Written as ds_write_b128
+    // itself: as a plain store the compiler cannot tell it from the DMA
+    // loads in flight into the same stage buffers and waits for every one
+    // before it (vmcnt 0), which drains the prefetch at each stage. It never
+    // overlaps them: it writes weight rows, the DMA token rows, and the loads
+    // into its own buffer have been waited for (wait_next). The barrier that
+    // follows waits for it (lgkmcnt 0) before any wave reads the stage.
+    auto lds_store16 = [](int8_t* p, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+      typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+      const uint32_t addr = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+      const u4v d = {a0, a1, a2, a3};
+      asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(d) : "memory");
     };
     // 4 int8 codes -> 4 fp16 (exact): bytes b + 128 under the exponent of
     // 1024 give 1024 + b + 128, minus 1152
@@ -643,50 +667,79 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
         }
       }
       int8_t* row = stages + (st % DNB) * Cfg::STAGE_BYTES + ra * BK;
-      *reinterpret_cast<uint4*>(row + (((2 * hf) ^ key_a) << 4)) = make_uint4(h[0], h[1], h[2], h[3]);
-      *reinterpret_cast<uint4*>(row + (((2 * hf + 1) ^ key_a) << 4)) = make_uint4(h[4], h[5], h[6], h[7]);
+      lds_store16(row + (((2 * hf) ^ key_a) << 4), h[0], h[1], h[2], h[3]);
+      lds_store16(row + (((2 * hf + 1) ^ key_a) << 4), h[4], h[5], h[6], h[7]);
     };
     const std::integral_constant<bool, true> f16{};
-    // step st: its weight registers and token DMA have landed (only stage
-    // st + 1's loads may be in flight), weights to LDS, barrier (stage st
-    // visible; every wave is done with stage st - 1, whose buffer the loads of
-    // stage st + 2 then take), the loads of stage st + 2, the MFMAs of st.
-    auto dstep = [&](int st, int set) __attribute__((always_inline)) {
-      const bool more = st + 1 < S;
-      if (wide) {
-        if (more) wait_vmcnt<2 + DLB>(); else wait_vmcnt<0>();
-      } else {
-        if (more) wait_vmcnt<1 + DLB>(); else wait_vmcnt<0>();
-      }
-      const uint32_t word = s_dbm[st];
-      write_a(st, set, word);
-      lds_barrier();
-      if (st + 2 < S) {
-        load_a(st + 2, set);
-        load_b(st + 2);
-      }
-      if (word) {
-        const int8_t* base = stages + (st % DNB) * Cfg::STAGE_BYTES;
+    auto read_stage = [&](int st, int fset) {
+      const int8_t* base = stages + (st % DNB) * Cfg::STAGE_BYTES;
 #pragma unroll
-        for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, 0);
-#pragma unroll
-        for (int m = 0; m < Cfg::NMFMA; ++m) mfma_one(m, 0, f16);
-      }
+      for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, fset);
     };
-    lds_barrier();   // the bitmap copy is in LDS (read by every step)
-    load_a(0, 0);
-    load_b(0);
-    if (S > 1) {
-      load_a(1, 1);
-      load_b(1);
+    // loads per step: the weight registers (one or two), the token DMA
+    // (DLB); stage st+1's are followed by those of stages st+2 and st+3
+    auto wait_next = [&]() {
+      if (wide) wait_vmcnt<2 * (2 + DLB)>(); else wait_vmcnt<2 * (1 + DLB)>();
+    };
+    // With one wave per SIMD (the 128 x 128 tiles) the fragments of stage
+    // st+1 are read while the MFMAs of stage st run (two register sets);
+    // with two (the 256 x 256 tiles) the other wave covers the reads, and a
+    // stage's fragments are read just before its MFMAs, which keeps the
+    // registers within two waves' share.
+    constexpr bool DBF = Cfg::WAVES_M != 4;
+    // q: the register set of stage st+4 (= st mod 4); fragment set of stage
+    // st: st mod 2
+    uint32_t w_cur = 0, w_next = 0;   // bitmap words of stages st, st+1
+    auto dstep = [&](int st, auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      wait_next();
+      write_a(st + 1, (q + 1) & 3, w_next);
+      lds_barrier();
+      load_a(st + 4, q);
+      load_b(st + 4);
+      const uint32_t w_after = word_of(st + 2);
+      if constexpr (DBF) {
+        if (w_next) read_stage(st + 1, (q + 1) & 1);
+        if (w_cur) {
+#pragma unroll
+          for (int m = 0; m < Cfg::NMFMA; ++m) mfma_one(m, q & 1, f16);
+        }
+      } else {
+        if (w_cur) {
+          read_stage(st, 0);
+#pragma unroll
+          for (int m = 0; m < Cfg::NMFMA; ++m) mfma_one(m, 0, f16);
+        }
+      }
+      w_cur = w_next;
+      w_next = w_after;
+    };
+    // prologue: stages 0-3 in flight, stage 0's weights to LDS, its fragments
+    for (int st = 0; st < 4; ++st) {
+      load_a(st, st);
+      load_b(st);
     }
-    for (int st = 0; st < S; st += 2) {
-      dstep(st, 0);
-      if (st + 1 < S) dstep(st + 1, 1);
+    w_cur = word_of(0);
+    w_next = word_of(1);
+    if (wide) wait_vmcnt<3 * (2 + DLB)>(); else wait_vmcnt<3 * (1 + DLB)>();
+    write_a(0, 0, w_cur);
+    lds_barrier();
+    if constexpr (DBF)
+      if (w_cur) read_stage(0, 0);
+    const std::integral_constant<int, 0> q0{};
+    const std::integral_constant<int, 1> q1{};
+    const std::integral_constant<int, 2> q2{};
+    const std::integral_constant<int, 3> q3{};
+    // in fours (steps past the last stage find zeros and a bitmap word of
+    // 0: no reads, no MFMAs), so the register sets stay where they are
+    for (int st = 0; st < S; st += 4) {
+      dstep(st, q0);
+      dstep(st + 1, q1);
+      dstep(st + 2, q2);
+      dstep(st + 3, q3);
     }
     wait_vmcnt<0>();
   };
-
   // Prologue: the row / column factors are read into registers, then the
   // first four stages are issued with the chunk-0 outlier gathers between
   // stages 0-1 and 2-3; factors and gathers go to LDS after the main loop.
