@@ -21,22 +21,23 @@
 //                    (CB * SCB / 127) or fp16 weight columns ([HF-blog]
 //                    "Usage"; [Summary] steps 3-4).
 //
-// Block = 8 wavefronts in two roles. Waves 0-3 stream the block's 16-feature
+// Block = 12 wavefronts in two roles. Waves 0-3 stream the block's 16-feature
 // weight tiles straight from HBM into registers (in the operand layout of
 // v_mfma_i32_16x16x64_i8: waves split K in 256-byte chunks) and run the
-// MFMAs. Waves 4-7 do the X side and the epilogue. Every block does the X
+// MFMAs. Waves 4-11 do the X side and the epilogue. Every block does the X
 // side itself (X is at most 8 x 16384 fp16 and comes from L2): a weight
 // wave is held up issuing its loads until the memory system takes them,
 // about as long as the weight takes to stream, so an X side that shared its
 // waves started only when the weight had almost landed. Split, it runs while
 // the weight streams. The X waves' loads go out first (a barrier orders them
 // before the weight loads); all barriers are LDS-only, so none waits for
-// loads in flight.
+// loads in flight. Eight X waves, two per SIMD, cover each other's latencies
+// (4096 -> 4096: M = 1 8.0 -> 7.6 us, M = 4 10.9 -> 10.3 us against four).
 //
-// X side: X-wave thread t holds the 16-byte chunks t, t + 256, ... of every
+// X side: X-wave thread t holds the 16-byte chunks t, t + 512, ... of every
 // token row in registers, so each 8-column flag mask is its own maximum over
 // the rows, the outlier elements are masked out from its own bits, and the
-// row maxima and outlier counts need one exchange between the four X waves
+// row maxima and outlier counts need one exchange between the eight X waves
 // (after a barrier every X thread knows the row scales and its chunks'
 // positions in the ascending outlier column list). The codes go to LDS;
 // block 0 also writes the intermediates (bitmap, cols, n, sx, Xq, Xo) to the
@@ -55,9 +56,9 @@ namespace i8mm {
 
 namespace {
 
-constexpr int kDcThreads = 512;             // 8 wavefronts
+constexpr int kDcThreads = 768;             // 12 wavefronts
 constexpr int kDcWWaves = 4;                // waves 0-3: weight tiles and MFMAs
-constexpr int kDcXThreads = 256;            // waves 4-7: X side and epilogue
+constexpr int kDcXThreads = 512;            // waves 4-11: X side and epilogue
 constexpr int kDcFeat = 16;                 // output features per tile
 constexpr int kDcChunk = 256;               // K bytes per MFMA chunk
 constexpr int kDcBatch = 4;                 // chunks per wave held in registers at once
@@ -86,8 +87,8 @@ __host__ __device__ constexpr int dc_lds_bytes(int M, int K) {
   return dc_round16(M * dc_pitch(K)) + 4 * ((K + 31) / 32);
 }
 
-// X thread t holds the 16-byte chunks t, t + 256, ... (JC of them, K <= JC *
-// 2048) of each of the first MR token rows (M <= MR, MR * JC <= kDcXRegs).
+// X thread t holds the 16-byte chunks t, t + 512, ... (JC of them, K <= JC *
+// 4096) of each of the first MR token rows (M <= MR, MR * JC <= kDcXRegs).
 template <int MR, int JC>
 __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     const uint16_t* __restrict__ X, const int8_t* __restrict__ Wq, const float* __restrict__ sw,
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool wrole = wave < kDcWWaves;      // uniform per wave
-  const int xt = tid - kDcXThreads;         // X-side thread index (X waves)
+  const int xt = tid - kDcWWaves * kWave;   // X-side thread index (X waves)
   const int xw = wave - kDcWWaves;          // X wave index (X waves)
   const int nchunks = K / 8;                // 16-byte chunks of a row
   const int nwords = (K + 31) / 32;
@@ -321,27 +322,35 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       }
     }
   }
+  // Element e (0..7) of a 16-byte chunk: v_perm_b32 picks bytes 2(e%4),
+  // 2(e%4)+1 of words (x, y) and of (z, w), then e/4 chooses; no dynamic
+  // index into the registers of X.
+  auto pick_half = [](const uint4& t, int e) -> uint32_t {
+    const uint32_t h = (uint32_t)(e & 3) * 2u;
+    const uint32_t sel = 0x0c0c0000u | ((h + 1u) << 8) | h;
+    const uint32_t p01 = __builtin_amdgcn_perm(t.y, t.x, sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(t.w, t.z, sel);
+    return (e & 4) ? p23 : p01;
+  };
 #pragma unroll
   for (int j = 0; j < JC; ++j) {
-    if (om[j]) {   // (rare)
+    if (om[j]) {   // (rare) the set bits only
       const int c = xt + kDcXThreads * j;
       int pos = pos0[j];
+      for (uint32_t bits = om[j]; bits; bits &= bits - 1u) {
+        const int e = __builtin_ctz(bits);
+        const int col = c * 8 + e;
+        if (pos < kDcMaxOut) s_cols[pos] = col;
+        if (first) cols_g[pos] = col;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {   // (unrolled: e indexes the registers of X)
-        if ((om[j] >> e) & 1u) {
-          const int col = c * 8 + e;
-          if (pos < kDcMaxOut) s_cols[pos] = col;
-          if (first) cols_g[pos] = col;
-#pragma unroll
-          for (int m = 0; m < MR; ++m) {
-            if (m < M) {
-              const uint16_t v = (uint16_t)half_of(xr[m][j], e);
-              if (pos < kDcMaxOut) s_xo[m][pos] = v;
-              if (first) Xo_g[m * ld + pos] = v;
-            }
+        for (int m = 0; m < MR; ++m) {
+          if (m < M) {
+            const uint16_t v = (uint16_t)pick_half(xr[m][j], e);
+            if (pos < kDcMaxOut) s_xo[m][pos] = v;
+            if (first) Xo_g[m * ld + pos] = v;
           }
-          ++pos;
         }
+        ++pos;
       }
     }
   }
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
     if (!first_tile) load_factors(f0);
     first_tile = false;
-    if (staged && n > 0) {
+    if (staged && n > 0 && xt < 256) {   // 16 features x up to 32 columns
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int t = mt + 16 * s2;
@@ -449,13 +458,13 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
 }  // namespace
 
 bool decode_applies(int64_t M, int64_t K) {
-  // an X thread holds ceil(K / 2048) chunks of each of MR rows, MR * chunks
-  // <= kDcXRegs: K <= 16384 for M <= 4, 8192 for M <= 8. Beyond 8 tokens the
-  // X side, repeated by every block, outlasts the weight stream (16 tokens
-  // at 4096 -> 4096: 22 us in one launch against 15 us as separate kernels).
+  // an X thread holds ceil(K / 4096) chunks of each of MR rows: K <= 16384
+  // for M <= 4, 8192 for M <= 8. Beyond 8 tokens the X side, repeated by
+  // every block, outlasts the weight stream (16 tokens at 4096 -> 4096: 22 us
+  // in one launch against 15 us as separate kernels).
   if (M < 1 || M > kDcMaxTok || K < 16) return false;
   const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
-  return jc <= (M <= 4 ? 8 : 4);
+  return jc <= (M <= 4 ? 4 : 2);
 }
 
 hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, int64_t M,
@@ -469,17 +478,17 @@ hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, i
   return launch_decode_t<MR_, JC_>(X, Wq, sw, M, N, K, tau16, bias, Y, Wf, bitmap, cols, n_out, \
                                    sx, Xq, Xo, s)
   if (M == 1) {
+    if (jc <= 1) I8MM_DECODE(1, 1);
     if (jc <= 2) I8MM_DECODE(1, 2);
-    if (jc <= 4) I8MM_DECODE(1, 4);
-    I8MM_DECODE(1, 8);
+    I8MM_DECODE(1, 4);
   }
   if (M <= 4) {
+    if (jc <= 1) I8MM_DECODE(4, 1);
     if (jc <= 2) I8MM_DECODE(4, 2);
-    if (jc <= 4) I8MM_DECODE(4, 4);
-    I8MM_DECODE(4, 8);
+    I8MM_DECODE(4, 4);
   }
-  if (jc <= 2) I8MM_DECODE(8, 2);
-  I8MM_DECODE(8, 4);
+  if (jc <= 1) I8MM_DECODE(8, 1);
+  I8MM_DECODE(8, 2);
 #undef I8MM_DECODE
 }
 
