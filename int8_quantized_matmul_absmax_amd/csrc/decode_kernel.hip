@@ -1,6 +1,6 @@
 // The whole few-token layer in one launch: outlier-column detection, row
 // quantization of X, int8 matmul with int32 accumulation, dequantization,
-// fp16 outlier product and bias, for 1 <= M <= 8 tokens. At these sizes the
+// fp16 outlier product and bias, for 1 <= M <= 16 tokens. At these sizes the
 // layer is bound by streaming the int8 weight from HBM once; run as separate
 // kernels, the steps on X cost more in launches than the weight stream.
 //
@@ -25,7 +25,7 @@
 // weight tiles straight from HBM into registers (in the operand layout of
 // v_mfma_i32_16x16x64_i8: waves split K in 256-byte chunks) and run the
 // MFMAs. Waves 4-11 do the X side and the epilogue. Every block does the X
-// side itself (X is at most 8 x 16384 fp16 and comes from L2): a weight
+// side itself (X is at most 16 x 4096 or 4 x 16384 fp16 and comes from L2): a weight
 // wave is held up issuing its loads until the memory system takes them,
 // about as long as the weight takes to stream, so an X side that shared its
 // waves started only when the weight had almost landed. Split, it runs while
@@ -62,7 +62,7 @@ constexpr int kDcXThreads = 512;            // waves 4-11: X side and epilogue
 constexpr int kDcFeat = 16;                 // output features per tile
 constexpr int kDcChunk = 256;               // K bytes per MFMA chunk
 constexpr int kDcBatch = 4;                 // chunks per wave held in registers at once
-constexpr int kDcMaxTok = 8;
+constexpr int kDcMaxTok = 16;
 constexpr int kDcMaxOut = 32;               // outlier columns staged in LDS
 constexpr int kDcXRegs = 32;                // 16-byte X chunks an X thread holds
 constexpr int kDcPad = 16;                  // LDS row padding of the codes
@@ -459,12 +459,13 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
 
 bool decode_applies(int64_t M, int64_t K) {
   // an X thread holds ceil(K / 4096) chunks of each of MR rows: K <= 16384
-  // for M <= 4, 8192 for M <= 8. Beyond 8 tokens the X side, repeated by
-  // every block, outlasts the weight stream (16 tokens at 4096 -> 4096: 22 us
-  // in one launch against 15 us as separate kernels).
+  // for M <= 4, 8192 for M <= 8, 4096 for M <= 16. Every block repeats the
+  // X side, so it grows with M; at 16 tokens (4096 -> 4096) one launch still
+  // edges out the separate kernels (14.5 against 14.9 us; 12 tokens 12.6
+  // against 14.3 us).
   if (M < 1 || M > kDcMaxTok || K < 16) return false;
   const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
-  return jc <= (M <= 4 ? 4 : 2);
+  return jc <= (M <= 4 ? 4 : M <= 8 ? 2 : 1);
 }
 
 hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, int64_t M,
@@ -487,8 +488,11 @@ hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, i
     if (jc <= 2) I8MM_DECODE(4, 2);
     I8MM_DECODE(4, 4);
   }
-  if (jc <= 1) I8MM_DECODE(8, 1);
-  I8MM_DECODE(8, 2);
+  if (M <= 8) {
+    if (jc <= 1) I8MM_DECODE(8, 1);
+    I8MM_DECODE(8, 2);
+  }
+  I8MM_DECODE(16, 1);
 #undef I8MM_DECODE
 }
 

@@ -1,7 +1,7 @@
-"""The single-launch few-token layer: the layer calls take it for M <= 8
-tokens with K <= 16384 (M <= 4) or 8192 (M <= 8), the columns of X an X-side
-thread holds in registers; other few-token shapes (up to 64 tokens) take the
-separate kernels (also here).
+"""The single-launch few-token layer: the layer calls take it for M <= 16
+tokens with K <= 16384 (M <= 4), 8192 (M <= 8) or 4096 (M <= 16), the
+columns of X an X-side thread holds in registers; other few-token shapes (up
+to 64 tokens) take the separate kernels (also here).
 
 Against the oracle: every intermediate it writes to the workspace bit for
 bit (bitmap, cols, n, codes, scales, gathered outlier columns and their zero
@@ -32,18 +32,19 @@ CASES = {
     "m4_k16384": (4, 16384, 520, 10, True, False),
     "m5_k2064": (5, 2064, 300, 3, False, False),
     "m8_k8192_n40": (8, 8192, 257, 40, True, False),
-    "m9_k1040_separate": (9, 1040, 100, 20, False, False),
-    "m12_k2048_n40_separate": (12, 2048, 130, 40, True, False),
+    "m9_k1040": (9, 1040, 100, 20, False, False),
+    "m12_k2048_n40": (12, 2048, 130, 40, True, False),
     "m16_k4112_separate": (16, 4112, 200, 7, False, False),
     "m8_k4096_many_tiles": (8, 4096, 16400, 6, True, False),
-    "m16_k4096_many_tiles_separate": (16, 4096, 16400, 6, True, False),
+    "m16_k4096_many_tiles": (16, 4096, 16400, 6, True, False),
     "m3_k16": (3, 16, 64, 0, False, False),
     "m7_fp16w": (7, 4096, 300, 8, True, True),
-    "m16_fp16w_separate": (16, 4096, 300, 8, True, True),
+    "m16_fp16w": (16, 4096, 300, 8, True, True),
     "m2_fp16w_n33": (2, 4112, 333, 33, False, True),
     "m20_fp16w_separate": (20, 4096, 300, 8, True, True),
     "m24_k4096_separate": (24, 4096, 520, 6, True, False),
-    "m13_k4096_n40_separate": (13, 4096, 1000, 40, False, False),
+    "m10_k8192_separate": (10, 8192, 300, 12, False, False),
+    "m13_k4096_n40": (13, 4096, 1000, 40, False, False),
     "m1_k16384": (1, 16384, 700, 9, True, False),
 }
 
