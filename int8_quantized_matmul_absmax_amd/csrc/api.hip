@@ -272,6 +272,20 @@ int check_workspace(const char* fn, const void* workspace, size_t workspace_byte
   return I8MM_OK;
 }
 
+// Argument checks of the layer calls (all before any device work).
+int check_layer_args(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                     const float* sw, int64_t N, const uint16_t* bias, float threshold,
+                     const uint16_t* Y) {
+  I8MM_TRY(check_dims(fn, M, N, K));
+  if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
+  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
+  I8MM_TRY(check_ptr(fn, "Wq", Wq, N * K > 0));
+  I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
+  I8MM_TRY(check_ptr(fn, "bias", bias, false));
+  I8MM_TRY(check_ptr(fn, "Y", Y, M * N > 0));
+  return I8MM_OK;
+}
+
 // The whole layer after argument checks common to both weight modes. Wf: the
 // fp16 weight when the layer keeps one (its outlier columns feed the outlier
 // product), else nullptr (they are recovered from Wq, sw). quantize_w: write
@@ -280,13 +294,7 @@ int run_layer(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int
               const float* sw, int64_t N, const uint16_t* bias, float threshold, uint16_t* Y,
               void* workspace, size_t workspace_bytes, hipStream_t s, const uint16_t* Wf,
               bool quantize_w) {
-  I8MM_TRY(check_dims(fn, M, N, K));
-  if (std::isnan(threshold)) return fail(I8MM_EINVAL, "%s: threshold is NaN", fn);
-  I8MM_TRY(check_ptr(fn, "X", X, M * K > 0));
-  I8MM_TRY(check_ptr(fn, "Wq", Wq, N * K > 0));
-  I8MM_TRY(check_ptr(fn, "sw", sw, N > 0));
-  I8MM_TRY(check_ptr(fn, "bias", bias, false));
-  I8MM_TRY(check_ptr(fn, "Y", Y, M * N > 0));
+  I8MM_TRY(check_layer_args(fn, X, M, K, Wq, sw, N, bias, threshold, Y));
   int64_t off[7], off_part = 0, off_kbl = 0;
   layout(M, K, off, &off_part, &off_kbl);
   I8MM_TRY(check_workspace(fn, workspace, workspace_bytes, off));
@@ -415,7 +423,7 @@ int linear_int8_mixed_noalloc(const uint16_t* X, int64_t M, int64_t K, const int
                               const float* sw, int64_t N, const uint16_t* bias, float threshold,
                               uint16_t* Y, i8mm_stream_t stream) {
   const char* fn = "linear_int8_mixed_noalloc";
-  I8MM_TRY(check_dims(fn, M, N, K));
+  I8MM_TRY(check_layer_args(fn, X, M, K, Wq, sw, N, bias, threshold, Y));
   int64_t off[7];
   layout(M, K, off);
   if (off[6] > (int64_t)I8MM_NOALLOC_SCRATCH_BYTES)
@@ -424,6 +432,7 @@ int linear_int8_mixed_noalloc(const uint16_t* X, int64_t M, int64_t K, const int
                 "library's scratch; use linear_int8_mixed with a workspace",
                 fn, (long long)M, (long long)K, (long long)off[6],
                 (long long)I8MM_NOALLOC_SCRATCH_BYTES);
+  if (M == 0 || N == 0) return ok();
   I8MM_TRY(check_device());
   void* ws = nullptr;
   I8MM_TRY(scratch_address(fn, &ws));
