@@ -33,18 +33,23 @@
 // before the weight loads); all barriers are LDS-only, so none waits for
 // loads in flight. Eight X waves, two per SIMD, cover each other's latencies
 // (4096 -> 4096: M = 1 8.0 -> 7.6 us, M = 4 10.9 -> 10.3 us against four).
+// While the weight loads are being issued, the memory pipeline is full: an X
+// wave that issued a load or store then would be held with them, so the X
+// side touches memory only for X itself until the weight is on its way.
 //
 // X side: X-wave thread t holds the 16-byte chunks t, t + 512, ... of every
 // token row in registers, so each 8-column flag mask is its own maximum over
 // the rows, the outlier elements are masked out from its own bits, and the
 // row maxima and outlier counts need one exchange between the eight X waves
-// (after a barrier every X thread knows the row scales and its chunks'
-// positions in the ascending outlier column list). The codes go to LDS;
-// block 0 also writes the intermediates (bitmap, cols, n, sx, Xq, Xo) to the
-// workspace. Then, per tile, the X waves gather the tile's outlier weights
-// while the weight waves run the MFMAs (token fragments from the LDS codes,
-// rows padded so the 16 token rows of one read hit distinct banks), the
-// partial tiles meet in LDS, and the X waves write Y.
+// (through an LDS counter only they wait on; after it every X thread knows
+// the row scales and its chunks' positions in the ascending outlier column
+// list). The codes go to LDS. After the barrier that hands them to the
+// weight waves, the blocks write the intermediates (bitmap, cols, n, sx,
+// Xq, Xo) to the workspace from LDS, the codes shared out between blocks.
+// Then, per tile, the X waves gather the tile's outlier weights while the
+// weight waves run the MFMAs (token fragments from the LDS codes, rows
+// padded so the 16 token rows of one read hit distinct banks), the partial
+// tiles meet in LDS, and the X waves write Y.
 
 #include <atomic>
 #include <algorithm>
@@ -78,6 +83,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dc_rsrc(const void* base, uint
 
 __host__ __device__ constexpr int dc_round16(int v) { return (v + 15) / 16 * 16; }
 
+// int8 codes of 8 fp16 elements with the scale s, as the row quantizer forms
+// them: y = fl32(x * s), then y + 1.5 * 2^23 rounds to the nearest integer
+// with ties to even and its low byte is the two's complement code. The
+// product is taken as fma(x, s, +0), one mixed-precision instruction that
+// reads the fp16 half directly: x * s is exact before its one rounding
+// either way, and a -0 product becoming +0 does not change the code.
+__device__ __forceinline__ uint2 dc_codes8(const uint4& t, float s) {
+  const float magic = 12582912.0f;
+  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu));
+    const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+    r[2 * q] = __builtin_bit_cast(uint32_t, __builtin_fmaf((float)lo, s, 0.0f) + magic);
+    r[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_fmaf((float)hi, s, 0.0f) + magic);
+  }
+  const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u);
+  const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
+  const uint32_t hi01 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
+  return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                    __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+}
+
 // LDS row pitch of the int8 codes: K rounded up to 256 bytes, plus 16, so
 // the 16 token rows of one fragment read hit distinct banks.
 __host__ __device__ constexpr int dc_pitch(int K) { return (K + 255) / 256 * 256 + kDcPad; }
@@ -100,12 +130,13 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   constexpr int XW = kDcXThreads / kWave;   // X waves
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t red[kDcWWaves][16 * 16];
-  __shared__ float s_wo[kDcMaxOut][16];             // outlier weights, [t][j]
-  __shared__ uint16_t s_xo[kDcMaxTok][kDcMaxOut];   // outlier activations, [m][t]
+  __shared__ __attribute__((aligned(16))) float s_wo[16][kDcMaxOut + 4];   // outlier weights, [j][t]
+  __shared__ __attribute__((aligned(16))) uint16_t s_xo[kDcMaxTok][kDcMaxOut];   // outlier activations, [m][t]
   __shared__ float s_sx[kDcMaxTok];
   __shared__ int s_cols[kDcMaxOut];
   __shared__ int s_cnt[XW][JC];                     // outlier columns per X wave and j
   __shared__ uint32_t s_rmax[XW][kDcMaxTok];        // row maxima per X wave
+  __shared__ int s_xsync;                           // X waves past their flags
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,9 +156,12 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   const int seg = (lane >> 4) * 16;          // this lane's 16 bytes of each 64-byte k-slice
 
   // The two roles run separate code between the same sequence of barriers:
-  // B0 (the X loads are out), B1 (the X waves' flag words, counts and row
-  // maxima), B2 (codes, row factors and staged outlier columns), then two
-  // per tile (partial tiles and outlier weights in LDS; LDS free again).
+  // B0 (the X loads are out), B2 (codes, row factors and staged outlier
+  // columns), then two per tile (partial tiles and outlier weights in LDS;
+  // LDS free again). Between B0 and B2 the X waves exchange their flag
+  // words, counts and row maxima through a counter in LDS that only they
+  // wait on, so they do not wait for the weight waves, which are held up
+  // issuing their loads until the memory system takes them.
   if (wrole) {
     // ---- weight waves
     constexpr int kOob = 0x7ffffff0;
@@ -153,7 +187,6 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     lds_only_barrier();   // B0
     tile_rsrc((int64_t)blockIdx.x * kDcFeat);
     load_w(wave);
-    lds_only_barrier();   // B1
     lds_only_barrier();   // B2
     for (int64_t tile = blockIdx.x; tile * kDcFeat < N; tile += gridDim.x) {
       v4i32 acc = v4i32{0, 0, 0, 0};
@@ -195,22 +228,30 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   }
 
   // ---- X waves: X into registers, then the first tile's factors
+  // The X loads are unconditional (rows and chunks past the end are
+  // clamped; clamped chunks are masked out of every use below, rows m >= M
+  // are not used). The tile's factors are loaded per tile, the first tile's
+  // once the X side is done: no wait before then covers them, and the
+  // epilogue that needs them waits for the tile's weight anyway.
   uint4 xr[MR][JC];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
 #pragma unroll
     for (int j = 0; j < JC; ++j) {
-      const int c = xt + kDcXThreads * j;
-      xr[m][j] = (m < M && c < nchunks) ? ld16(X + (int64_t)m * K + c * 8) : make_uint4(0, 0, 0, 0);
+      const int c = min(xt + kDcXThreads * j, nchunks - 1);
+      xr[m][j] = ld16(X + (int64_t)min(m, M - 1) * K + c * 8);
     }
   }
-  float sw_f = 0.0f, bias_f = 0.0f;
+  float sw_f = 0.0f;
+  uint32_t bias_h = 0;
   auto load_factors = [&](int64_t f0) {
-    const int64_t f = f0 + jf;
-    sw_f = f < N ? sw[f] : 0.0f;
-    bias_f = (bias && f < N) ? h2f(bias[f]) : 0.0f;
+    const uint32_t nf = (uint32_t)min<int64_t>(kDcFeat, N - f0);
+    const __amdgpu_buffer_rsrc_t rs = dc_rsrc(sw + f0, nf * 4u);
+    const __amdgpu_buffer_rsrc_t rb = dc_rsrc(bias ? bias + f0 : nullptr, bias ? nf * 2u : 0u);
+    sw_f = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, jf * 4, 0, 0));
+    bias_h = __builtin_amdgcn_raw_buffer_load_b16(rb, jf * 2, 0, 0);
   };
-  load_factors((int64_t)blockIdx.x * kDcFeat);
+  if (xt == 0) s_xsync = 0;
   lds_only_barrier();   // B0
 
   // column flags (a thread holds whole columns, so each 8-column mask is its
@@ -219,15 +260,6 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
   // its wave, and the row maxima over the normal columns (outlier elements
   // masked out from the thread's own bits)
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  auto strip = [&](uint32_t bits, const uint4& t) -> uint4 {
-    uint32_t h[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t b = bits >> (2 * q);
-      h[q] &= ((b & 1u) ? 0u : 0x0000ffffu) | ((b & 2u) ? 0u : 0xffff0000u);
-    }
-    return make_uint4(h[0], h[1], h[2], h[3]);
-  };
   uint32_t om[JC];   // outlier bits of chunk j (bit e: element e)
   int excl[JC];      // outlier columns before chunk j's within the wave
 #pragma unroll
@@ -257,12 +289,30 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     word |= (uint32_t)__shfl_xor((int)word, 2, kWave);
     if ((c & 3) == 0 && c < nchunks) {
       sbm[c >> 2] = word;
-      if (first) bitmap_g[c >> 2] = word;
     }
     const int cnt = __popc(om[j]);
     const int incl = wave_inclusive_scan(cnt, lane);
     excl[j] = incl - cnt;
     if (lane == kWave - 1) s_cnt[xw][j] = incl;
+  }
+  // per chunk: the magnitude bits of its normal elements (outlier elements
+  // and sign bits cleared), and byte masks that clear the outlier codes
+  uint32_t amk[JC][4], bmk[JC][2];
+#pragma unroll
+  for (int j = 0; j < JC; ++j) {
+    const bool cv = xt + kDcXThreads * j < nchunks;   // not a clamped chunk
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t b = om[j] >> (2 * q);
+      amk[j][q] = cv ? ((b & 1u) ? 0u : 0x00007fffu) | ((b & 2u) ? 0u : 0x7fff0000u) : 0u;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t k = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k |= ((om[j] >> (4 * h + e)) & 1u) ? 0u : 0xffu << (8 * e);
+      bmk[j][h] = k;
+    }
   }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -270,17 +320,27 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       u16x2 m2 = u16x2{0, 0};
 #pragma unroll
       for (int j = 0; j < JC; ++j) {
-        const uint4 t = strip(om[j], xr[m][j]);
-        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+        const uint32_t w[4] = {xr[m][j].x, xr[m][j].y, xr[m][j].z, xr[m][j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+          m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & amk[j][i]));
       }
       const uint32_t mxw = wave_max_u32_dpp(m2[0] > m2[1] ? m2[0] : m2[1]);
       if (lane == 0) s_rmax[xw][m] = mxw;
     }
   }
-  lds_only_barrier();   // B1
+  // the X waves' exchange: each arrives once its LDS writes are done, and
+  // waits until all eight have (every X wave reaches each exchange; the
+  // counter only grows, so exchange e waits for e * 8 arrivals)
+  auto x_exchange = [&](int e) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (lane == 0) __hip_atomic_fetch_add(&s_xsync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(&s_xsync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < e * XW)
+      __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+  };
+  x_exchange(1);
 
   // positions (chunk order: j, then X wave, then lane), codes, outlier
   // columns and activations
@@ -299,26 +359,32 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     n += tot;
   }
   const int64_t ld = ((int64_t)n + 31) / 32 * 32;
+  // row factors: lane m of every X wave combines the X waves' maxima of row
+  // m; each row's scale then comes from lane m (readlane), one division per
+  // lane instead of one per row
+  float sc_l = 0.0f;
+  if (lane < M) {
+    uint32_t mx = s_rmax[0][lane];
+#pragma unroll
+    for (int w = 1; w < XW; ++w) mx = mx > s_rmax[w][lane] ? mx : s_rmax[w][lane];
+    const float a = h2f(mx);
+    sc_l = a != 0.0f ? 127.0f / a : 0.0f;
+    if (xw == 0) s_sx[lane] = a;
+  }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m < M) {
-      uint32_t mx = s_rmax[0][m];
-#pragma unroll
-      for (int w = 1; w < XW; ++w) mx = mx > s_rmax[w][m] ? mx : s_rmax[w][m];
-      const float a = h2f(mx);
-      const float sc = a != 0.0f ? 127.0f / a : 0.0f;
+      const float sc = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), m));
 #pragma unroll
       for (int j = 0; j < JC; ++j) {
         const int c = xt + kDcXThreads * j;
         if (c < nchunks) {
-          const uint2 q = codes8_rne(strip(om[j], xr[m][j]), sc);
+          uint2 q = dc_codes8(xr[m][j], sc);
+          q.x &= bmk[j][0];
+          q.y &= bmk[j][1];
           *reinterpret_cast<uint2*>(s_xq + m * ldx + c * 8) = q;
-          if (first) *reinterpret_cast<uint2*>(Xq_g + (int64_t)m * K + c * 8) = q;
         }
-      }
-      if (xt == 0) {
-        s_sx[m] = a;
-        if (first) sx_g[m] = a;
       }
     }
   }
@@ -341,46 +407,102 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
         const int e = __builtin_ctz(bits);
         const int col = c * 8 + e;
         if (pos < kDcMaxOut) s_cols[pos] = col;
-        if (first) cols_g[pos] = col;
+        else if (first) cols_g[pos] = col;   // (more than fit in LDS)
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
           if (m < M) {
             const uint16_t v = (uint16_t)pick_half(xr[m][j], e);
             if (pos < kDcMaxOut) s_xo[m][pos] = v;
-            if (first) Xo_g[m * ld + pos] = v;
+            else if (first) Xo_g[m * ld + pos] = v;
           }
         }
         ++pos;
       }
     }
   }
-  if (first) {
-    if (xt == 0) *n_g = n;
+  // The first tile's factors and outlier weights are requested now, once
+  // every outlier column is in LDS (a second exchange): the loads wait in
+  // the memory pipeline behind the weight loads, as the weight waves do
+  // before B2, and each gathered byte arrives with its own line of the
+  // weight stream rather than after all of it.
+  const bool staged = n <= kDcMaxOut;
+  uint32_t raw[2] = {0u, 0u};
+  auto gather_issue = [&](int64_t f0) {
+    if (staged && n > 0 && xt < 256) {   // 16 features x up to 32 columns
+      // bounded buffer loads; a slot past n or a row past N reads 0 and is
+      // not stored
+      const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
+      const __amdgpu_buffer_rsrc_t rwo =
+          Wf ? dc_rsrc(Wf + f0 * K, (uint32_t)rows_w * (uint32_t)K * 2u)
+             : dc_rsrc(Wq + f0 * K, (uint32_t)rows_w * (uint32_t)K);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int t = mt + 16 * s2;
+        const bool ok = t < n && jf < rows_w;
+        const int off = ok ? jf * K + s_cols[t] : 0x3ffffff0;
+        raw[s2] = Wf ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rwo, off * 2, 0, 0)
+                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rwo, off, 0, 0);
+      }
+    }
+  };
+  x_exchange(2);
+  load_factors((int64_t)blockIdx.x * kDcFeat);
+  gather_issue((int64_t)blockIdx.x * kDcFeat);
+  lds_only_barrier();   // B2
+
+  // The workspace intermediates go out only now, from LDS: until the weight
+  // waves have issued their loads, the memory pipeline is full and a store
+  // holds its wave until it is taken. Every block holds the same codes, so
+  // block b writes the code chunks c = b, b + G, ... of every row; block 0
+  // writes the rest (the outlier columns and activations past the first 32
+  // went out above).
+  {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int per = b < nchunks ? (nchunks - b + G - 1) / G : 0;
 #pragma unroll 1
-    for (int64_t i = xt; i < (int64_t)M * (ld - n); i += kDcXThreads) {
-      const int64_t m = i / (ld - n);
-      Xo_g[m * ld + n + (i - m * (ld - n))] = 0;
+    for (int i = xt; i < M * per; i += kDcXThreads) {
+      const int m = i / per, c = b + G * (i - m * per);
+      *reinterpret_cast<uint2*>(Xq_g + (int64_t)m * K + c * 8) =
+          *reinterpret_cast<const uint2*>(s_xq + m * ldx + c * 8);
+    }
+    if (first) {
+#pragma unroll 1
+      for (int w = xt; w < nwords; w += kDcXThreads) bitmap_g[w] = sbm[w];
+      if (xt < M) sx_g[xt] = s_sx[xt];
+      if (xt == 0) *n_g = n;
+      const int ns = min(n, kDcMaxOut);
+#pragma unroll 1
+      for (int i = xt; i < M * ns; i += kDcXThreads) {
+        const int m = i / ns, t = i - m * ns;
+        if (m == 0) cols_g[t] = s_cols[t];
+        Xo_g[m * ld + t] = s_xo[m][t];
+      }
+#pragma unroll 1
+      for (int64_t i = xt; i < (int64_t)M * (ld - n); i += kDcXThreads) {
+        const int64_t m = i / (ld - n);
+        Xo_g[m * ld + n + (i - m * (ld - n))] = 0;
+      }
     }
   }
-  lds_only_barrier();   // B2
 
   // per tile: the tile's outlier weights while the weight waves run the
   // MFMAs, then Y
-  const bool staged = n <= kDcMaxOut;
   bool first_tile = true;
   for (int64_t tile = blockIdx.x; tile * kDcFeat < N; tile += gridDim.x) {
     const int64_t f0 = tile * kDcFeat;
     const int rows_w = (int)min<int64_t>(kDcFeat, N - f0);
-    if (!first_tile) load_factors(f0);
+    if (!first_tile) {
+      load_factors(f0);
+      gather_issue(f0);
+    }
     first_tile = false;
-    if (staged && n > 0 && xt < 256) {   // 16 features x up to 32 columns
+    if (staged && n > 0 && xt < 256) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int t = mt + 16 * s2;
-        if (t < n && jf < rows_w) {
-          const int64_t off = (f0 + jf) * K + s_cols[t];
-          s_wo[t][jf] = Wf ? h2f(Wf[off]) : h2f(f2h(((float)Wq[off] * sw_f) / 127.0f));
-        }
+        if (t < n && jf < rows_w)
+          s_wo[jf][t] = Wf ? h2f(raw[s2])
+                           : h2f(f2h(((float)(int8_t)(uint8_t)raw[s2] * sw_f) / 127.0f));
       }
     }
     lds_only_barrier();   // partial tiles and outlier weights in LDS
@@ -393,7 +515,15 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       const float y = (float)acc_s * (s_sx[mt] / 127.0f) * fw;
       float yo = 0.0f;
       if (staged) {
-        for (int t = 0; t < n; ++t) yo += h2f(s_xo[mt][t]) * s_wo[t][jf];
+        // four columns per step (one read of each side), summed in order
+        for (int t = 0; t < n; t += 4) {
+          const uint2 xo4 = *reinterpret_cast<const uint2*>(&s_xo[mt][t]);
+          const float4 wo4 = *reinterpret_cast<const float4*>(&s_wo[jf][t]);
+          yo += h2f(xo4.x & 0xffffu) * wo4.x;
+          if (t + 1 < n) yo += h2f(xo4.x >> 16) * wo4.y;
+          if (t + 2 < n) yo += h2f(xo4.y & 0xffffu) * wo4.z;
+          if (t + 3 < n) yo += h2f(xo4.y >> 16) * wo4.w;
+        }
       } else {
         // ascending outlier columns straight from the bitmap, X and W
         for (int w = 0; w < nwords; ++w) {
@@ -407,7 +537,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
           }
         }
       }
-      Y[(int64_t)mt * N + f] = f2h(y + yo + bias_f);
+      Y[(int64_t)mt * N + f] = f2h(y + yo + h2f(bias_h));
     }
     lds_only_barrier();   // the next tile rewrites red and s_wo
   }

@@ -87,3 +87,32 @@ def test_decode_layer(gpu, case):
         Y2 = ops.int8_mm_dequant(Xq, Wqd, sx, swd, Xo, cols, n, bd)
         torch.cuda.synchronize()
         assert np.array_equal(host(Y).view(np.uint16), host(Y2).view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_subnormal_rows(gpu, M):
+    """Token rows of fp16 subnormals: the row scale is 127 / a for a
+    subnormal a, and every code comes from a subnormal times that scale."""
+    note("decode subnormal M=%d" % M)
+    ops = gpu.ops
+    K, N = 4096, 256
+    rng = np.random.default_rng(900 + M)
+    X = synth.normal_f16(rng, (M, K), 1.0)
+    synth.plant_outlier_columns(rng, X, 5, 7.0, 20.0, 1.0)
+    bits = rng.integers(1, 0x400, size=(K,), dtype=np.uint16)
+    bits |= rng.integers(0, 2, size=(K,), dtype=np.uint16) << 15
+    X[0] = bits.view(np.float16)      # row 0: subnormals only (no outliers in it)
+    if M > 2:
+        X[2, ::5] = np.float16(6e-8)
+    W = synth.normal_f16(rng, (N, K), 0.02)
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0, None)
+    ws = torch.empty((ops.workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    Y = ops.linear_int8_mixed(dev(X), dev(Wq), dev(sw), None, 6.0, ws)
+    torch.cuda.synchronize()
+    views = ops.workspace_views(ws, M, K)
+    _check_intermediates(gpu, views, X, ref)
+    assert np.count_nonzero(ref["Xq"][0]) > K // 2   # the subnormal row has real codes
+    err = y_err(host(Y), ref["Y"])
+    assert err <= Y_TOL, err
+

@@ -128,7 +128,15 @@ def test_outlier_detect_empty_rows(gpu):
 
 # ------------------------------------------------------------------ a3: rows of X
 
-@pytest.mark.parametrize("case", ["tiny", "medium", "no_bitmap"])
+def _subnormal_rows(rng, X, rows):
+    """Rows made of fp16 subnormals (exponent field 0, random sign), so that
+    a row's absmax and every product x * s come from subnormal inputs."""
+    bits = rng.integers(1, 0x400, size=(len(rows), X.shape[1]), dtype=np.uint16)
+    bits |= (rng.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15)
+    X[rows] = bits.view(np.float16)
+
+
+@pytest.mark.parametrize("case", ["tiny", "medium", "no_bitmap", "subnormal"])
 def test_rowwise_quant_bitexact(gpu, case):
     note("rowwise %s" % case)
     if case == "tiny":
@@ -136,6 +144,10 @@ def test_rowwise_quant_bitexact(gpu, case):
     else:
         X = synth.opt_ffn_up(M=257, K=4096, N=16)["X"]
     X[1, :] = 0
+    if case == "subnormal":
+        rng = np.random.default_rng(77)
+        _subnormal_rows(rng, X, [0, 2, 100, 256])
+        X[3, ::7] = np.float16(6e-8)    # subnormal elements in a normal row
     if case == "no_bitmap":
         cols = np.zeros(0, np.int32)
         bm = None
