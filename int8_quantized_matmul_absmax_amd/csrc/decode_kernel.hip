@@ -35,7 +35,8 @@
 // (4096 -> 4096: M = 1 8.0 -> 7.6 us, M = 4 10.9 -> 10.3 us against four).
 // While the weight loads are being issued, the memory pipeline is full: an X
 // wave that issued a load or store then would be held with them, so the X
-// side touches memory only for X itself until the weight is on its way.
+// side touches memory only for X itself until it has the codes (by then the
+// weight is on its way).
 //
 // X side: X-wave thread t holds the 16-byte chunks t, t + 512, ... of every
 // token row in registers, so each 8-column flag mask is its own maximum over
@@ -46,10 +47,11 @@
 // list). The codes go to LDS. After the barrier that hands them to the
 // weight waves, the blocks write the intermediates (bitmap, cols, n, sx,
 // Xq, Xo) to the workspace from LDS, the codes shared out between blocks.
-// Then, per tile, the X waves gather the tile's outlier weights while the
-// weight waves run the MFMAs (token fragments from the LDS codes, rows
-// padded so the 16 token rows of one read hit distinct banks), the partial
-// tiles meet in LDS, and the X waves write Y.
+// Per tile, the X waves gather the tile's outlier weights (the first tile's
+// requested just before that barrier) while the weight waves run the MFMAs
+// (token fragments from the LDS codes, rows padded so the 16 token rows of
+// one read hit distinct banks), the partial tiles meet in LDS, and the X
+// waves write Y.
 
 #include <atomic>
 #include <algorithm>
