@@ -490,7 +490,8 @@ def _traffic_from_counters(section):
 # ---------------------------------------------------------------- profiling mode
 
 PROFILE_SECTIONS = ("copy_probe", "ffn175b_weight_quant", "ffn175b_layer", "opt6.7b_layer",
-                    "decode_m1", "decode_m4", "decode_m16", "mlp_n32_layer2")
+                    "decode_m1", "decode_m4", "decode_m16", "mlp_n32_layer2",
+                    "mlp_n32_layer2_room_all")
 
 
 def _profile_kernels():
@@ -591,6 +592,14 @@ def _profile_kernels():
     ws2 = torch.empty((ops.workspace_bytes(M, F, H),), dtype=torch.uint8, device="cuda")
     Y2 = torch.empty((M, H), dtype=torch.float16, device="cuda")
     section("mlp_n32_layer2")
+    for _ in range(2):
+        ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2)
+    end()
+    # the same layer with room in the workspace for every outlier column
+    del ws2
+    ws2 = torch.empty((ops.workspace_bytes_all_outliers(M, F, H),), dtype=torch.uint8,
+                      device="cuda")
+    section("mlp_n32_layer2_room_all")
     for _ in range(2):
         ops.linear_int8_mixed(G, Wq2, sw2, None, 6.0, ws2, Y2)
     end()
