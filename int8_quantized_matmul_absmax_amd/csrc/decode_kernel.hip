@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     return;
   }
 
-  // ---- X waves: X into registers, then the first tile's factors
+  // ---- X waves: X into registers
   // The X loads are unconditional (rows and chunks past the end are
   // clamped; clamped chunks are masked out of every use below, rows m >= M
   // are not used). The tile's factors are loaded per tile, the first tile's
