@@ -592,8 +592,8 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
 bool decode_applies(int64_t M, int64_t K) {
   // an X thread holds ceil(K / 4096) chunks of each of MR rows: K <= 16384
   // for M <= 4, 8192 for M <= 8, 4096 for M <= 16. Every block repeats the
-  // X side, so it grows with M; at 16 tokens (4096 -> 4096) one launch still
-  // edges out the separate kernels (14.5 against 14.9 us; 12 tokens 12.6
+  // X side, so it grows with M; at 16 tokens (4096 -> 4096) one launch
+  // takes 11.2 us against 14.9 us for the separate kernels (12 tokens: 10.4
   // against 14.3 us).
   if (M < 1 || M > kDcMaxTok || K < 16) return false;
   const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
