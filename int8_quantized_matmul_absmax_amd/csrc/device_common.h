@@ -10,6 +10,8 @@ typedef int32_t v4i32 __attribute__((ext_vector_type(4)));
 typedef int32_t v16i32 __attribute__((ext_vector_type(16)));
 typedef float v16f32 __attribute__((ext_vector_type(16)));
 typedef _Float16 v8f16 __attribute__((ext_vector_type(8)));
+typedef _Float16 v4f16 __attribute__((ext_vector_type(4)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 

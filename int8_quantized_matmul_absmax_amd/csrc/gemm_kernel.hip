@@ -19,16 +19,19 @@
 // holds only the int8 weight; taken from the fp16 weight when it keeps one).
 //
 // Mapping onto the matrix cores. Both operands are K-contiguous (Xq [M, K],
-// Wq [N, K]). v_mfma_i32_32x32x32_i8 takes a 32 x 32-byte slice of each: the
-// "A" operand is a 32-row slice of Wq (output features), the "B" operand a
-// 32-row slice of Xq (tokens). A lane's 16 accumulators then hold 4 runs of 4
+// Wq [N, K]). v_mfma_i32_16x16x64_i8 takes a 16 x 64-byte slice of each (a
+// whole stage of K): the "A" operand is a 16-row slice of Wq (output
+// features), the "B" operand a 16-row slice of Xq (tokens); lane l holds 16
+// bytes of row l % 16 at k group l / 16. A lane's 4 accumulators then hold 4
 // consecutive output features of one token. A and B fragments use the same
 // lane -> k assignment, so the sum over k is the same whatever order the
-// instruction uses inside its 32-byte slice (integer sums are exact).
+// instruction uses inside its slice (integer sums are exact). The same work
+// as v_mfma_i32_32x32x32_i8 tiles ran 4-6% faster on these 16 x 16 tiles
+// (175B shape 1952 -> 1867 us, OPT shape 119.5 -> 112 us, Y bit-identical).
 //
 // Block = 8 wavefronts, two per SIMD, in a 2 x 4 grid over a BN x BM
-// (features x tokens) tile; each wave owns a (BN/2) x (BM/4) sub-tile (4 x 2
-// MFMA tiles of 32 x 32 for 256 x 256, 128 accumulator registers), so while
+// (features x tokens) tile; each wave owns a (BN/2) x (BM/4) sub-tile (8 x 4
+// MFMA tiles of 16 x 16 for 256 x 256, 128 accumulator registers), so while
 // one wave of a SIMD waits on LDS or a barrier the other issues MFMAs. Small
 // grids (fewer 256 x 256 tiles than CUs) use 128 x 128 tiles of 4 waves.
 // K advances in BK = 64-byte stages through a ring of five LDS buffers (all
@@ -46,21 +49,22 @@
 //
 // LDS layout of one stage: rows of BK = 64 bytes (Wq rows first, then Xq
 // rows); 16-byte chunk c of row r sits at position c ^ f(r), f(r) =
-// (r >> 2) & 3. A fragment read (lane l < 32 at row l, lane l + 32 at the
-// same row, next chunk) then completes in the minimum number of LDS cycles;
-// the bank-conflict counter reads zero for it, as it does for 16-byte reads
-// of consecutive addresses. Measured alternatives: with no swizzle such a
-// read takes 3.9x the cycles; with f(r) = ((r >> 1) ^ (r >> 3)) & 3 it takes
-// 1.95x. The layout only permutes which chunk each lane's DMA load fetches:
-// every row is still read as one 64-byte segment and written to LDS in order.
+// (r >> 2) & 3. A fragment read (lane l at row l % 16, logical chunk l / 16)
+// then places every 8 consecutive lanes in distinct banks, as 16-byte reads
+// of consecutive addresses do. (For the 32 x 32 tiles' read, lane l < 32 at
+// row l and lane l + 32 at the next chunk of the same row, the
+// bank-conflict counter read zero with this key; with no swizzle such a
+// read took 3.9x the cycles, with f(r) = ((r >> 1) ^ (r >> 3)) & 3 1.95x.)
+// The layout only permutes which chunk each lane's DMA load fetches: every
+// row is still read as one 64-byte segment and written to LDS in order.
 //
 // Epilogue: per-tile dequantization with the row / column factors staged in
 // LDS; the fp16 outlier product (first 16 outlier columns: gathered in the
 // prologue, held in registers through the main loop, then staged in LDS;
-// further columns read per 16-column step) runs on v_mfma_f32_32x32x16_f16
-// onto the dequantized tile; lane swaps
-// (v_permlane32_swap) and a pass through LDS turn each pair of 32-feature
-// slices into whole 128-byte row segments of Y per 8 lanes.
+// further columns read per 16-column step) runs on v_mfma_f32_16x16x16_f16
+// onto the dequantized tile; a pass through LDS turns each four 16-feature
+// slices into whole 128-byte row segments of Y per 8 lanes. The outlier
+// segments run v_mfma_f32_16x16x32_f16 on the same fragment layout.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin by block id; the id
 // is remapped so each XCD owns a contiguous range of tiles, rastered in groups
@@ -91,9 +95,9 @@ struct GemmCfg {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M;           // tokens per wave
   static constexpr int WN = BN / WAVES_N;           // features per wave
-  static constexpr int TM = WM / 32;                // MFMA tiles per wave, token dim
-  static constexpr int TN = WN / 32;                // MFMA tiles per wave, feature dim
-  static constexpr int KS = BK / 32;                // MFMA k-steps per stage
+  static constexpr int TM = WM / 16;                // MFMA tiles per wave, token dim
+  static constexpr int TN = WN / 16;                // MFMA tiles per wave, feature dim
+  static constexpr int KS = BK / 64;                // MFMA k-steps per stage
   static constexpr int CPR = BK / 16;               // 16-byte chunks per LDS row
   static constexpr int ROWS = BM + BN;              // LDS rows per stage
   static constexpr int STAGE_BYTES = ROWS * BK;
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int wn = wave % Cfg::WAVES_N, wm = wave / Cfg::WAVES_N;
-  const int l32 = lane & 31, lhi = lane >> 5;
+  const int l16 = lane & 15, lq = lane >> 4;   // MFMA operand row, 16-byte k group
 
   int tile_m, tile_n;
   tile_of_block((M + BM - 1) / BM, (N + BN - 1) / BN, tile_m, tile_n);
@@ -386,26 +390,26 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   int aoff[KS][TN], boff[KS][TM];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 2 + lhi;
+    const int c = ks * 4 + lq;
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
-      const int r = wn * WN + a * 32 + l32;
+      const int r = wn * WN + a * 16 + l16;
       aoff[ks][a] = r * BK + ((c ^ swz_key(r)) << 4);
     }
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
-      const int r = BN + wm * WM + b * 32 + l32;
+      const int r = BN + wm * WM + b * 16 + l16;
       boff[ks][b] = r * BK + ((c ^ swz_key(r)) << 4);
     }
   }
 
-  v16i32 acc[TN][TM];
+  v4i32 acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
     for (int b = 0; b < TM; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
+      for (int r = 0; r < 4; ++r) acc[a][b][r] = 0;
 
   v4i32 fa[2][KS][TN], fb[2][KS][TM];
   // Fragment r of a stage, in the order the MFMAs of a step consume them:
@@ -425,17 +429,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, set);
   };
   // MFMA m of a step: k-step ks, A tile a, B tile b. The outlier segment
-  // reads the same 16-byte fragments as 8 fp16 values (16 k per MFMA instead
-  // of 32) and keeps its fp32 sums in the same accumulator registers.
+  // reads the same 16-byte fragments as 8 fp16 values (32 k per MFMA instead
+  // of 64) and keeps its fp32 sums in the same accumulator registers.
   auto mfma_one = [&](int m, int set, auto f16) {
     const int ks = m / (TN * TM), a = (m / TM) % TN, b = m % TM;
     if constexpr (decltype(f16)::value) {
-      const v16f32 r = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+      const v4f32 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           __builtin_bit_cast(v8f16, fa[set][ks][a]), __builtin_bit_cast(v8f16, fb[set][ks][b]),
-          __builtin_bit_cast(v16f32, acc[a][b]), 0, 0, 0);
-      acc[a][b] = __builtin_bit_cast(v16i32, r);
+          __builtin_bit_cast(v4f32, acc[a][b]), 0, 0, 0);
+      acc[a][b] = __builtin_bit_cast(v4i32, r);
     } else {
-      acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[set][ks][a], fb[set][ks][b],
+      acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[set][ks][a], fb[set][ks][b],
                                                         acc[a][b], 0, 0, 0);
     }
   };
@@ -505,17 +509,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
 
-  // sw/127 (and bias) of the 16 features lane (l32, lhi) holds in slice a.
+  // sw/127 (and bias) of the 4 features lane (l16, lq) holds in slice a.
   auto load_fw = [&](int a, float* fw, float* bv) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int fl = wn * WN + a * 32 + 8 * g + 4 * lhi;
-      const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
-      fw[4 * g] = f4.x; fw[4 * g + 1] = f4.y; fw[4 * g + 2] = f4.z; fw[4 * g + 3] = f4.w;
-      if (bv) {
-        const float4 b4 = *reinterpret_cast<const float4*>(s_bias + fl);
-        bv[4 * g] = b4.x; bv[4 * g + 1] = b4.y; bv[4 * g + 2] = b4.z; bv[4 * g + 3] = b4.w;
-      }
+    const int fl = wn * WN + a * 16 + 4 * lq;
+    const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
+    fw[0] = f4.x; fw[1] = f4.y; fw[2] = f4.z; fw[3] = f4.w;
+    if (bv) {
+      const float4 b4 = *reinterpret_cast<const float4*>(s_bias + fl);
+      bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
     }
   };
 
@@ -784,20 +785,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     // whole dequantized value, as the compact segment does.
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
-      float fw[16];
+      float fw[4];
       load_fw(a, fw, nullptr);
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        const float ax = s_ax[wm * WM + b * 32 + l32];
-        v16f32 y;
+        const float ax = s_ax[wm * WM + b * 16 + l16];
+        v4f32 y;
         if (dense && Wf == nullptr) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax;
+          for (int r = 0; r < 4; ++r) y[r] = (float)acc[a][b][r] * ax;
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) y[r] = (float)acc[a][b][r] * ax * fw[r];
+          for (int r = 0; r < 4; ++r) y[r] = (float)acc[a][b][r] * ax * fw[r];
         }
-        acc[a][b] = __builtin_bit_cast(v16i32, y);
+        acc[a][b] = __builtin_bit_cast(v4i32, y);
       }
     }
     if constexpr (!dense) {
@@ -821,69 +822,56 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   if (Y) lds_barrier();
 
   // ---- epilogue
-  // Lane (l32, lhi), accumulator r of tile (a, b):
-  //   token   = m0 + wm*WM + b*32 + l32
-  //   feature = n0 + wn*WN + a*32 + 8*(r/4) + 4*lhi + (r%4)
+  // Lane (l16, lq), accumulator r of tile (a, b) (the D layout of the 16 x 16
+  // MFMAs):
+  //   token   = m0 + wm*WM + b*16 + l16
+  //   feature = n0 + wn*WN + a*16 + 4*lq + r
   if (WITH_C) {
     const bool n4 = (N & 3) == 0;
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        const int64_t tok = m0 + wm * WM + b * 32 + l32;
+        const int64_t tok = m0 + wm * WM + b * 16 + l16;
         if (tok >= M) continue;
+        const int64_t f = n0 + wn * WN + a * 16 + 4 * lq;
+        int32_t* dst = C + tok * N + f;
+        if (n4 && f + 3 < N) {
+          *reinterpret_cast<int4*>(dst) =
+              make_int4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t f = n0 + wn * WN + a * 32 + 8 * g + 4 * lhi;
-          int32_t* dst = C + tok * N + f;
-          if (n4 && f + 3 < N) {
-            *reinterpret_cast<int4*>(dst) =
-                make_int4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
-                          acc[a][b][4 * g + 3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (f + e < N) dst[e] = acc[a][b][4 * g + e];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (f + e < N) dst[e] = acc[a][b][e];
         }
       }
   }
   if (!Y) return;
 
   // ---- fp16 output
-  // Two 32-feature slices at a time go through this wave's part of the (now
-  // idle) stage buffers: after packing to fp16, lanes l and l+32 hold
-  // features 8g + 0..3 and 8g + 4..7 of group g; v_permlane32_swap on groups
-  // (g, g+1) gives lane l all 8 features of group g and lane l+32 all 8 of
-  // group g+1, written to LDS as 16-byte pieces of [token][64 features] rows.
-  // They are read back row-contiguous, so 8 consecutive lanes store one whole
-  // 128-byte row segment of Y: write misses reach memory as full lines
-  // rather than as 16-byte pieces of 32 different rows.
+  // Four 16-feature slices at a time go through this wave's part of the (now
+  // idle) stage buffers: lane (l16, lq) packs its 4 features of token
+  // b*16 + l16 to fp16 and writes them as 8 bytes of a [token][64 features]
+  // row. The rows are read back contiguously, so 8 consecutive lanes store
+  // one whole 128-byte row segment of Y: write misses reach memory as full
+  // lines rather than as 8-byte pieces of 16 different rows.
   constexpr int OUT_ROW = Cfg::OUT_ROW;
-  static_assert(TN % 2 == 0, "slices are stored in pairs");
+  static_assert(TN % 4 == 0, "slices are stored in fours");
   int8_t* s_out = lds + Cfg::OUT0 + wave * (WM * OUT_ROW);
   const bool n8 = (N & 7) == 0;
-  auto stage_tile = [&](int a, int b, const v16f32& y) {
-    uint32_t p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = f2h(y[2 * i]) | (f2h(y[2 * i + 1]) << 16);
-#pragma unroll
-    for (int gp = 0; gp < 4; gp += 2) {
-      // p[2gp], p[2gp+1]: group gp; p[2gp+2], p[2gp+3]: group gp+1
-      const auto s0 = __builtin_amdgcn_permlane32_swap(p[2 * gp], p[2 * gp + 2], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(p[2 * gp + 1], p[2 * gp + 3], false, false);
-      const int row = b * 32 + l32;
-      const int col = (a & 1) * 64 + 16 * (gp + lhi);   // byte offset in the row
-      *reinterpret_cast<uint4*>(s_out + row * OUT_ROW + col) =
-          make_uint4(s0[0], s1[0], s0[1], s1[1]);
-    }
+  auto stage_tile = [&](int a, int b, const v4f32& y) {
+    const uint32_t p0 = f2h(y[0]) | (f2h(y[1]) << 16);
+    const uint32_t p1 = f2h(y[2]) | (f2h(y[3]) << 16);
+    const int row = b * 16 + l16;
+    const int col = (a & 3) * 32 + 8 * lq;   // byte offset in the row
+    *reinterpret_cast<uint2*>(s_out + row * OUT_ROW + col) = make_uint2(p0, p1);
   };
-  auto flush_pair = [&](int a0) {
-    // a0 even: slices a0, a0+1 = features wn*WN + a0*32 + [0, 64)
+  auto flush_four = [&](int a0) {
+    // a0 = 4i: slices a0 .. a0+3 = features wn*WN + a0*16 + [0, 64)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int64_t f = n0 + wn * WN + a0 * 32 + 8 * (lane & 7);
+    const int64_t f = n0 + wn * WN + a0 * 16 + 8 * (lane & 7);
 #pragma unroll 4
     for (int it = 0; it < WM / 8; ++it) {
       const int row = it * 8 + (lane >> 3);
@@ -907,13 +895,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // LDS outlier fragments: 8 fp16 (t = 8*lhi .. 8*lhi+7) of row l32 of a
-  // 32-row slice; same lane -> t assignment on the weight and token side.
-  auto wo_frag = [&](int a) -> v8f16 {
-    return *reinterpret_cast<const v8f16*>(s_wo + (wn * WN + a * 32 + l32) * 16 + lhi * 8);
+  // LDS outlier fragments of v_mfma_f32_16x16x16_f16: 4 fp16 (t = 4*lq ..
+  // 4*lq+3) of row l16 of a 16-row slice; the same lane -> t assignment on
+  // the weight and the token side.
+  auto wo_frag = [&](int a) -> v4f16 {
+    return *reinterpret_cast<const v4f16*>(s_wo + (wn * WN + a * 16 + l16) * 16 + lq * 4);
   };
-  auto xo_frag = [&](int b) -> v8f16 {
-    return *reinterpret_cast<const v8f16*>(s_xo + (wm * WM + b * 32 + l32) * 16 + lhi * 8);
+  auto xo_frag = [&](int b) -> v4f16 {
+    return *reinterpret_cast<const v4f16*>(s_xo + (wm * WM + b * 16 + l16) * 16 + lq * 4);
   };
 
   // Fragments of outlier chunks beyond the first (more than 16 outlier
@@ -921,13 +910,13 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // from Wf when the weight is kept in fp16, else recovered from Wq as
   // fp16(fl32(fl32(q * sw) / 127)); the activations are read from Xo. Slow,
   // but it keeps the per-slice register footprint small.
-  auto wo_frag_g = [&](int a, int t0) -> v8f16 {
-    v8f16 w;
-    const int64_t f = n0 + wn * WN + a * 32 + l32;
+  auto wo_frag_g = [&](int a, int t0) -> v4f16 {
+    v4f16 w;
+    const int64_t f = n0 + wn * WN + a * 16 + l16;
     const float swf = f < N ? sw[f] : 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + lhi * 8 + e;
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + lq * 4 + e;
       if (Wf) {
         w[e] = (t < n_o && f < N) ? __builtin_bit_cast(_Float16, Wf[f * K + cols[t]])
                                   : (_Float16)0.0f;
@@ -939,61 +928,61 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
     return w;
   };
-  auto xo_frag_g = [&](int b, int t0) -> v8f16 {
-    const int64_t tok = m0 + wm * WM + b * 32 + l32;
-    if (tok >= M) return v8f16{};
-    return __builtin_bit_cast(v8f16, ld16(Xo + tok * ldo + t0 + lhi * 8));
+  auto xo_frag_g = [&](int b, int t0) -> v4f16 {
+    const int64_t tok = m0 + wm * WM + b * 16 + l16;
+    if (tok >= M) return v4f16{};
+    return __builtin_bit_cast(v4f16, *reinterpret_cast<const uint2*>(Xo + tok * ldo + t0 + lq * 4));
   };
 
-  // One 32-feature slice a at a time, its TM token tiles in VGPRs: dequantize
+  // One 16-feature slice a at a time, its TM token tiles in VGPRs: dequantize
   // y = C * (sx/127) * (sw/127), add the fp16 outlier product on
-  // v_mfma_f32_32x32x16_f16 (first 16 columns from the LDS-staged fragments,
+  // v_mfma_f32_16x16x16_f16 (first 16 columns from the LDS-staged fragments,
   // further chunks from global memory), add the bias, store.
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
-    float fw[16], bv[16];
+    float fw[4], bv[4];
     load_fw(a, fw, bias ? bv : nullptr);
-    v16f32 y[TM];
+    v4f32 y[TM];
     if (seg2) {
       // already dequantized, with the outlier product added (dense: still
       // without the factor sw/127)
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        y[b] = __builtin_bit_cast(v16f32, acc[a][b]);
+        y[b] = __builtin_bit_cast(v4f32, acc[a][b]);
         if (dense && Wf == nullptr) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) y[b][r] = y[b][r] * fw[r];
+          for (int r = 0; r < 4; ++r) y[b][r] = y[b][r] * fw[r];
         }
       }
     } else {
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        const float ax = s_ax[wm * WM + b * 32 + l32];
+        const float ax = s_ax[wm * WM + b * 16 + l16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
+        for (int r = 0; r < 4; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
       }
     }
     if (n_o > 0 && !seg2) {
-      const v8f16 wa = wo_frag(a);
+      const v4f16 wa = wo_frag(a);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        y[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xo_frag(b), y[b], 0, 0, 0);
+        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, xo_frag(b), y[b], 0, 0, 0);
     }
     for (int t0 = 16; t0 < (seg2 ? 0 : n_o); t0 += 16) {
-      const v8f16 wa = wo_frag_g(a, t0);
+      const v4f16 wa = wo_frag_g(a, t0);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        y[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xo_frag_g(b, t0), y[b], 0, 0, 0);
+        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, xo_frag_g(b, t0), y[b], 0, 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
       if (bias) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[b][r] += bv[r];
+        for (int r = 0; r < 4; ++r) y[b][r] += bv[r];
       }
       stage_tile(a, b, y[b]);
     }
-    if (a & 1) flush_pair(a - 1);
+    if ((a & 3) == 3) flush_four(a - 3);
   }
 }
 
