@@ -23,6 +23,13 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
+// Two narrowing conversions at once (lo in bits 0-15, hi in 16-31): one
+// v_cvt_pk_f16_f32, with the same rounding as f2h.
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+typedef _Float16 v2f16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2h2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f32{lo, hi}, v2f16));
+}
 
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);

@@ -510,7 +510,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
 
-  // sw/127 (and bias) of the 4 features lane (l16, lq) holds in slice a.
+  // sw/127 and the bias (-0.0 without one) of the 4 features lane (l16, lq)
+  // holds in slice a.
   auto load_fw = [&](int a, float* fw, float* bv) {
     const int fl = wn * WN + a * 16 + 4 * lq;
     const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
@@ -750,7 +751,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       keep[8] = __builtin_bit_cast(uint32_t, sx[m0 + hr]);
     } else {
       keep[8] = __builtin_bit_cast(uint32_t, sw[n0 + hr]);
-      if (bias) keep[9] = bias[n0 + hr];
+      // without a bias, -0.0: adding it leaves every value as it is
+      keep[9] = bias ? bias[n0 + hr] : 0x8000u;
     }
   }
   // The outlier gathers go after stages 0-1 and before stages 2-3: the first
@@ -861,8 +863,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   int8_t* s_out = lds + Cfg::OUT0 + wave * (WM * OUT_ROW);
   const bool n8 = (N & 7) == 0;
   auto stage_tile = [&](int a, int b, const v4f32& y) {
-    const uint32_t p0 = f2h(y[0]) | (f2h(y[1]) << 16);
-    const uint32_t p1 = f2h(y[2]) | (f2h(y[3]) << 16);
+    const uint32_t p0 = f2h2(y[0], y[1]);
+    const uint32_t p1 = f2h2(y[2], y[3]);
     const int row = b * 16 + l16;
     const int col = (a & 3) * 32 + 8 * lq;   // byte offset in the row
     *reinterpret_cast<uint2*>(s_out + row * OUT_ROW + col) = make_uint2(p0, p1);
@@ -873,22 +875,38 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t f = n0 + wn * WN + a0 * 16 + 8 * (lane & 7);
-#pragma unroll 4
-    for (int it = 0; it < WM / 8; ++it) {
-      const int row = it * 8 + (lane >> 3);
-      const uint4 v = *reinterpret_cast<const uint4*>(s_out + row * OUT_ROW + 16 * (lane & 7));
-      const int64_t tok = m0 + wm * WM + row;
-      if (tok < M) {
-        uint16_t* dst = Y + tok * N + f;
-        if (n8 && f + 7 < N) {
-          // streaming store: Y is written once and not read back by this
-          // kernel, so it should not displace operand lines in the caches
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
-        } else {
+    // Streaming stores: Y is written once and not read back by this kernel,
+    // so it should not displace operand lines in the caches.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // (uniform) every row and feature of the 64-wide slab in range: all the
+    // rows are read from LDS first, then stored, so that the stores do not
+    // each wait for their own read
+    const bool whole = n8 && n0 + wn * WN + a0 * 16 + 64 <= N && m0 + wm * WM + WM <= M;
+    if (whole) {
+      u32x4 v[WM / 8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (f + e < N) dst[e] = (uint16_t)half_of(v, e);
+      for (int it = 0; it < WM / 8; ++it)
+        v[it] = *reinterpret_cast<const u32x4*>(s_out + (it * 8 + (lane >> 3)) * OUT_ROW +
+                                                16 * (lane & 7));
+      uint16_t* dst = Y + (m0 + wm * WM + (lane >> 3)) * N + f;
+#pragma unroll
+      for (int it = 0; it < WM / 8; ++it)
+        __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst + (int64_t)it * 8 * N));
+    } else {
+#pragma unroll 4
+      for (int it = 0; it < WM / 8; ++it) {
+        const int row = it * 8 + (lane >> 3);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_out + row * OUT_ROW + 16 * (lane & 7));
+        const int64_t tok = m0 + wm * WM + row;
+        if (tok < M) {
+          uint16_t* dst = Y + tok * N + f;
+          if (n8 && f + 7 < N) {
+            __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (f + e < N) dst[e] = (uint16_t)half_of(v, e);
+          }
         }
       }
     }
@@ -942,7 +960,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     float fw[4], bv[4];
-    load_fw(a, fw, bias ? bv : nullptr);
+    load_fw(a, fw, bv);
     v4f32 y[TM];
     if (seg2) {
       // already dequantized, with the outlier product added (dense: still
@@ -977,10 +995,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
-      if (bias) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[b][r] += bv[r];
-      }
+      for (int r = 0; r < 4; ++r) y[b][r] += bv[r];
       stage_tile(a, b, y[b]);
     }
     if ((a & 3) == 3) flush_four(a - 3);

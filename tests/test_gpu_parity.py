@@ -194,6 +194,75 @@ def test_int32_accumulators_extremes(gpu):
     assert int(np.abs(C_ref).max()) == K * 127 * 127
 
 
+# ------------------------------------------------------------------ a7: the fp32 dequantize order
+
+def _dequant_fp32(C, sx, sw, bias):
+    """fp16(fl32(fl32(fl32(C) * fl32(sx / 127)) * fl32(sw / 127)) + bias) in
+    IEEE single precision (numpy's float32 operations round to nearest even,
+    as does its float32 -> float16 conversion): the order in which every
+    kernel forms an output with no outlier column. The oracle's fp64 value
+    only bounds this within the 1e-3 bar; this pins the fp32 arithmetic and
+    the final rounding bit for bit."""
+    ax = sx.astype(np.float32) / np.float32(127.0)
+    fw = sw.astype(np.float32) / np.float32(127.0)
+    with np.errstate(over="ignore"):
+        y = (C.astype(np.float32) * ax[:, None]) * fw[None, :]
+        if bias is not None:
+            y = y + bias.astype(np.float32)[None, :]
+        return y.astype(np.float16)
+
+
+# (M, N, K, bias): 256 x 256 tiles with ragged token and feature tiles, with
+# whole ones only, 128 x 128 tiles with N not a multiple of 8, few-token GEMV
+DEQUANT_CASES = {
+    "large_ragged": (1000, 16392, 128, False),
+    "large_whole_bias": (1024, 16384, 192, True),
+    "small_n_odd_bias": (300, 1003, 272, True),
+    "gemv": (40, 520, 1040, False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DEQUANT_CASES))
+def test_dequant_fp32_order(gpu, case):
+    """int8_mm_dequant without outlier columns against the fp32 expression,
+    with scales over six decades so that outputs reach the fp16 subnormals
+    and overflow to infinity."""
+    M, N, K, with_bias = DEQUANT_CASES[case]
+    note("dequant fp32 order %s" % case)
+    rng = np.random.default_rng(4400 + M + N)
+    Xq = synth.random_codes(M + 11, (M, K))
+    Wq = synth.random_codes(N + 13, (N, K))
+    sx = np.exp(rng.uniform(np.log(1e-4), np.log(1e3), M)).astype(np.float32)
+    sw = np.exp(rng.uniform(np.log(1e-3), np.log(1e2), N)).astype(np.float32)
+    b = synth.normal_f16(rng, (N,), 0.5) if with_bias else None
+    Y = _ops(gpu).int8_mm_dequant(dev(Xq), dev(Wq), dev(sx), dev(sw),
+                                  bias=None if b is None else dev(b))
+    torch.cuda.synchronize()
+    Y_ref = _dequant_fp32(O.int32_accumulators(Xq, Wq), sx, sw, b)
+    tiny = (Y_ref != 0) & (np.abs(Y_ref) < np.float16(6.1e-5))   # fp16 subnormals
+    assert np.isinf(Y_ref).any() and tiny.any()
+    assert np.array_equal(host(Y).view(np.uint16), Y_ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 40, 520])
+def test_layer_dequant_fp32_order(gpu, M):
+    """The whole layer on X without outlier columns (the single-launch decode
+    for 1 and 8 tokens, the GEMV for 40, the tiled GEMM for 520): Y equals
+    the fp32 expression over the oracle's codes and scales bit for bit."""
+    note("layer dequant fp32 order M=%d" % M)
+    K, N = 4096, 1000
+    rng = np.random.default_rng(4500 + M)
+    X = np.clip(synth.normal_f16(rng, (M, K), 1.0).astype(np.float32), -5.0, 5.0).astype(np.float16)
+    W = synth.normal_f16(rng, (N, K), 0.02)
+    b = synth.normal_f16(rng, (N,), 0.5) if M % 2 == 0 else None
+    Wq, sw = O.quantize_weight_rows(W)
+    ref = O.linear_int8_mixed(X, Wq, sw, 6.0, b)
+    assert ref["n"] == 0
+    Y, _ = _run_linear(gpu, X, Wq, sw, bias=b)
+    Y_ref = _dequant_fp32(ref["C"], ref["sx"], sw, b)
+    assert np.array_equal(Y.view(np.uint16), Y_ref.view(np.uint16))
+
+
 # ------------------------------------------------------------------ whole layer
 
 def _run_linear(gpu, X, Wq_ref, sw_ref, tau=6.0, bias=None):
