@@ -957,10 +957,34 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // y = C * (sx/127) * (sw/127), add the fp16 outlier product on
   // v_mfma_f32_16x16x16_f16 (first 16 columns from the LDS-staged fragments,
   // further chunks from global memory), add the bias, store.
+  // The LDS values a slice uses are read one slice ahead (the token-side ones
+  // once): the compiler cannot move these reads past the staging stores of
+  // the slice before, so read at the slice itself each would wait for its
+  // own LDS round trip.
+  const bool o_lds = n_o > 0 && !seg2;
+  float ax_b[TM];
+  v4f16 xo_b[TM];
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    ax_b[b] = s_ax[wm * WM + b * 16 + l16];
+    xo_b[b] = o_lds ? xo_frag(b) : v4f16{};
+  }
+  float fw_n[4], bv_n[4];
+  load_fw(0, fw_n, bv_n);
+  v4f16 wa_n = o_lds ? wo_frag(0) : v4f16{};
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     float fw[4], bv[4];
-    load_fw(a, fw, bv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      fw[r] = fw_n[r];
+      bv[r] = bv_n[r];
+    }
+    const v4f16 wa_lds = wa_n;
+    if (a + 1 < TN) {
+      load_fw(a + 1, fw_n, bv_n);
+      if (o_lds) wa_n = wo_frag(a + 1);
+    }
     v4f32 y[TM];
     if (seg2) {
       // already dequantized, with the outlier product added (dense: still
@@ -976,16 +1000,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     } else {
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
-        const float ax = s_ax[wm * WM + b * 16 + l16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[b][r] = (float)acc[a][b][r] * ax * fw[r];
+        for (int r = 0; r < 4; ++r) y[b][r] = (float)acc[a][b][r] * ax_b[b] * fw[r];
       }
     }
-    if (n_o > 0 && !seg2) {
-      const v4f16 wa = wo_frag(a);
+    if (o_lds) {
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, xo_frag(b), y[b], 0, 0, 0);
+        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa_lds, xo_b[b], y[b], 0, 0, 0);
     }
     for (int t0 = 16; t0 < (seg2 ? 0 : n_o); t0 += 16) {
       const v4f16 wa = wo_frag_g(a, t0);
