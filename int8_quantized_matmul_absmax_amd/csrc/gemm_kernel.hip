@@ -510,8 +510,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
   };
 
-  // sw/127 and the bias (-0.0 without one) of the 4 features lane (l16, lq)
-  // holds in slice a.
+  // sw/127 (and the bias) of the 4 features lane (l16, lq) holds in slice a.
   auto load_fw = [&](int a, float* fw, float* bv) {
     const int fl = wn * WN + a * 16 + 4 * lq;
     const float4 f4 = *reinterpret_cast<const float4*>(s_fw + fl);
@@ -751,8 +750,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       keep[8] = __builtin_bit_cast(uint32_t, sx[m0 + hr]);
     } else {
       keep[8] = __builtin_bit_cast(uint32_t, sw[n0 + hr]);
-      // without a bias, -0.0: adding it leaves every value as it is
-      keep[9] = bias ? bias[n0 + hr] : 0x8000u;
+      if (bias) keep[9] = bias[n0 + hr];
     }
   }
   // The outlier gathers go after stages 0-1 and before stages 2-3: the first
@@ -960,69 +958,80 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // The LDS values a slice uses are read one slice ahead (the token-side ones
   // once): the compiler cannot move these reads past the staging stores of
   // the slice before, so read at the slice itself each would wait for its
-  // own LDS round trip.
-  const bool o_lds = n_o > 0 && !seg2;
-  float ax_b[TM];
-  v4f16 xo_b[TM];
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    ax_b[b] = s_ax[wm * WM + b * 16 + l16];
-    xo_b[b] = o_lds ? xo_frag(b) : v4f16{};
-  }
-  float fw_n[4], bv_n[4];
-  load_fw(0, fw_n, bv_n);
-  v4f16 wa_n = o_lds ? wo_frag(0) : v4f16{};
-#pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    float fw[4], bv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      fw[r] = fw_n[r];
-      bv[r] = bv_n[r];
-    }
-    const v4f16 wa_lds = wa_n;
-    if (a + 1 < TN) {
-      load_fw(a + 1, fw_n, bv_n);
-      if (o_lds) wa_n = wo_frag(a + 1);
-    }
-    v4f32 y[TM];
-    if (seg2) {
-      // already dequantized, with the outlier product added (dense: still
-      // without the factor sw/127)
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        y[b] = __builtin_bit_cast(v4f32, acc[a][b]);
-        if (dense && Wf == nullptr) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[b][r] = y[b][r] * fw[r];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[b][r] = (float)acc[a][b][r] * ax_b[b] * fw[r];
-      }
-    }
-    if (o_lds) {
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa_lds, xo_b[b], y[b], 0, 0, 0);
-    }
-    for (int t0 = 16; t0 < (seg2 ? 0 : n_o); t0 += 16) {
-      const v4f16 wa = wo_frag_g(a, t0);
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, xo_frag_g(b, t0), y[b], 0, 0, 0);
-    }
+  // own LDS round trip. The loop is instantiated with and without the bias
+  // add, chosen by a uniform branch on the argument, so that without a bias
+  // no instruction is spent on it.
+  auto slices = [&](auto with_bias) __attribute__((always_inline)) {
+    constexpr bool WB = decltype(with_bias)::value;
+    const bool o_lds = n_o > 0 && !seg2;
+    float ax_b[TM];
+    v4f16 xo_b[TM];
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[b][r] += bv[r];
-      stage_tile(a, b, y[b]);
+      ax_b[b] = s_ax[wm * WM + b * 16 + l16];
+      xo_b[b] = o_lds ? xo_frag(b) : v4f16{};
     }
-    if ((a & 3) == 3) flush_four(a - 3);
-  }
+    float fw_n[4], bv_n[4];
+    load_fw(0, fw_n, WB ? bv_n : nullptr);
+    v4f16 wa_n = o_lds ? wo_frag(0) : v4f16{};
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      float fw[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        fw[r] = fw_n[r];
+        bv[r] = WB ? bv_n[r] : 0.0f;
+      }
+      const v4f16 wa_lds = wa_n;
+      if (a + 1 < TN) {
+        load_fw(a + 1, fw_n, WB ? bv_n : nullptr);
+        if (o_lds) wa_n = wo_frag(a + 1);
+      }
+      v4f32 y[TM];
+      if (seg2) {
+        // already dequantized, with the outlier product added (dense: still
+        // without the factor sw/127)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+          y[b] = __builtin_bit_cast(v4f32, acc[a][b]);
+          if (dense && Wf == nullptr) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[b][r] = y[b][r] * fw[r];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[b][r] = (float)acc[a][b][r] * ax_b[b] * fw[r];
+        }
+      }
+      if (o_lds) {
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa_lds, xo_b[b], y[b], 0, 0, 0);
+      }
+      for (int t0 = 16; t0 < (seg2 ? 0 : n_o); t0 += 16) {
+        const v4f16 wa = wo_frag_g(a, t0);
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          y[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(wa, xo_frag_g(b, t0), y[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        if constexpr (WB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[b][r] += bv[r];
+        }
+        stage_tile(a, b, y[b]);
+      }
+      if ((a & 3) == 3) flush_four(a - 3);
+    }
+  };
+  if (bias)
+    slices(std::integral_constant<bool, true>{});
+  else
+    slices(std::integral_constant<bool, false>{});
 }
 
 template <class Cfg>
