@@ -424,7 +424,9 @@ def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y, label):
     (Wq_gpu, host copy) bit for bit."""
     import numpy as np
     from oracle import llm_int8 as O
+    t0 = time.perf_counter()
     Wq_ref, sw_ref = O.quantize_weight_rows(d["W"])
+    t_wquant = time.perf_counter() - t0
     ref = O.linear_int8_mixed(d["X"], Wq_ref, sw_ref, 6.0, rows=rows_y)
     Yr = np.asarray(ref["Y"], np.float64)
     dY = np.abs(np.asarray(Y_rows, np.float64) - Yr)
@@ -458,6 +460,23 @@ def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y, label):
         calls += 1
     dt = total / calls
     tops = 2.0 * rows.size * N * K / dt / 1e12
+    # the tiny config (16 x 256 -> 256) on one thread: the whole layer call,
+    # weight quantization included, best of 20
+    tiny_ms = None
+    try:
+        from threadpoolctl import threadpool_limits
+        from int8_quantized_matmul_absmax_amd import synth
+        t = synth.tiny()
+        with threadpool_limits(limits=1):
+            best = float("inf")
+            for _ in range(20):
+                t0 = time.perf_counter()
+                Wq_t, sw_t = O.quantize_weight_rows(t["W"])
+                O.linear_int8_mixed(t["X"], Wq_t, sw_t, 6.0)
+                best = min(best, time.perf_counter() - t0)
+        tiny_ms = round(best * 1e3, 3)
+    except ImportError:
+        pass
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -469,6 +488,10 @@ def _cpu_baseline(d, M, N, K, target_s, Wq_gpu, Y_rows, rows_y, label):
              "sample": "%d of %d token rows x all %d outputs of the %s layer (outlier "
                        "detection over all rows; weight quantization outside the timing), "
                        "%d call(s), %.2f s each" % (rows.size, M, N, label, calls, dt),
+             "weight_quant_s": round(t_wquant, 3),
+             "weight_quant_note": "the oracle's per-row weight quantization of the whole "
+                                  "[%d x %d] weight, once, same threads" % (N, K),
+             "tiny_16x256x256_single_thread_ms": tiny_ms,
              "host": {"cpu_model": model, "logical_cpus": os.cpu_count(),
                       "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}, parity)
 
