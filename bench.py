@@ -22,7 +22,8 @@ Prints ONE JSON line (N=1):
                 HIP events on the launch stream
   cpu_baseline  the CPU oracle timed on this host on a bounded row sample
   extras        the OPT-6.7B FFN-up layer; decode M = 1, 4, 16 (weight rotated
-                beyond 2 x MALL, HIP-graph timed); the activation side and the
+                beyond 2 x MALL, HIP-graph timed); the tiny 16 x 256 -> 256
+                layer's per-call cost, eager and HIP-graph; the activation side and the
                 one-time weight quantization against HBM (inputs rotated
                 beyond 2 x MALL); the two-layer MLP outlier-density sweep; a
                 plain device copy's bandwidth (the measured HBM ceiling)
@@ -339,6 +340,41 @@ def _measure_decode(ops):
     res["timing"] = ("hip graph of many calls, replayed; weight rotated over copies beyond "
                      "2 x MALL; warm: one weight copy")
     return res
+
+
+def _measure_tiny(ops):
+    """The tiny layer (16 x 256 -> 256, one launch of the few-token kernel):
+    what a call costs when there is almost no work. Timed eagerly (HIP events
+    around 200 calls on the current stream, host launch overhead included)
+    and from a HIP graph of 50 calls (GPU time only)."""
+    import torch
+    from int8_quantized_matmul_absmax_amd import synth
+    d = synth.tiny()
+    X = torch.from_numpy(d["X"]).cuda()
+    Wq, sw = ops.int8_quantize_colwise_weight(torch.from_numpy(d["W"]).cuda())
+    M, K = X.shape
+    N = Wq.shape[0]
+    ws = torch.empty((ops.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def call():
+        return ops.linear_int8_mixed(X, Wq, sw, None, 6.0, ws, Y)
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(200):
+        call()
+    end.record()
+    end.synchronize()
+    eager = start.elapsed_time(end) * 1e3 / 200
+    us_g, same = _graph_time_us(call, reps=50)
+    return {"M": M, "K": K, "N": N, "us_eager_per_call": round(eager, 3),
+            "us_graph_per_call": round(us_g, 3), "replays_identical": bool(same),
+            "timing": "eager: hip events around 200 calls (launch overhead included); "
+                      "graph: 50 calls per graph, replayed"}
 
 
 def _measure_mlp(ops, prewarm_ms, stream):
@@ -989,6 +1025,8 @@ def main():
         log("decode")
         extras["decode_4096x4096"] = _measure_decode(ops)
         torch.cuda.empty_cache()
+        log("tiny layer")
+        extras["tiny_16x256x256"] = _measure_tiny(ops)
         log("mlp sweep")
         extras["mlp_sweep"] = _measure_mlp(ops, args.prewarm_ms, stream)
         torch.cuda.empty_cache()
