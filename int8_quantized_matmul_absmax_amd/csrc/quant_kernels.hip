@@ -95,7 +95,15 @@ __global__ __launch_bounds__(256) void k_outlier_flags(const uint16_t* __restric
     const uint4 v3 = ld16(base + (r + 12) * K);
     fold_abs8(mx, v0); fold_abs8(mx, v1); fold_abs8(mx, v2); fold_abs8(mx, v3);
   }
-  for (; r < r1; r += 4) fold_abs8(mx, ld16(base + r * K));
+  if (r < r1) {
+    // the last rows in one round trip: slots past the end read the block's
+    // last row again (a duplicate leaves the maximum as it is)
+    uint4 v[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) v[i] = ld16(base + min(r + 4 * i, r1 - 1) * K);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) fold_abs8(mx, v[i]);
+  }
   uint32_t mask = flag_mask8(mx, tau16);
   if (!col_ok) mask = 0;   // (with threshold 0 an empty max would pass)
   uint32_t word = mask << (col0 & 31);
@@ -143,7 +151,17 @@ __global__ __launch_bounds__(256) void k_outlier_flag_bands(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < 8; ++i) fold_abs8(mx, v[i]);
   }
-  for (; r < r1; r += 16) fold_abs8(mx, ld16(base + r * K));
+  if (r < r1) {
+    // the band's last partial batch, in one round trip as well: its rows past
+    // the band's end read the band's last row again (a row of the band read
+    // twice leaves the maximum as it is). One load at a time, these took a
+    // memory round trip each.
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ld16(base + min(r + 16 * i, r1 - 1) * K);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fold_abs8(mx, v[i]);
+  }
   uint32_t mask = flag_mask8(mx, tau16);
   if (!col_ok || r0 >= M) mask = 0;   // (with threshold 0 an empty max would pass)
   // the four rows of a wavefront at one column slot, then the 4 slots of a word
