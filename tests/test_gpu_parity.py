@@ -213,9 +213,11 @@ def _dequant_fp32(C, sx, sw, bias):
 
 
 # (M, N, K, bias): 256 x 256 tiles with ragged token and feature tiles, with
-# whole ones only, 128 x 128 tiles with N not a multiple of 8, few-token GEMV
+# N not a multiple of 8 (element stores), with whole ones only, 128 x 128
+# tiles with N not a multiple of 8, few-token GEMV
 DEQUANT_CASES = {
     "large_ragged": (1000, 16392, 128, False),
+    "large_n_odd_bias": (1030, 16388, 64, True),
     "large_whole_bias": (1024, 16384, 192, True),
     "small_n_odd_bias": (300, 1003, 272, True),
     "gemv": (40, 520, 1040, False),
