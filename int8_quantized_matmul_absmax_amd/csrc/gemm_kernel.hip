@@ -586,18 +586,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     auto load_a = [&](int st, int set) {
       const int col = st * 32 + 16 * hf;
       const bool ok = col < K;
-      if (wide) {
-        const int off = ok ? (ra * K + col) * 2 : 0x7fffffe0;
-        areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
-        areg[set][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off + 16, 0, 0));
-      } else {
-        const int off = ok ? ra * K + col : 0x7ffffff0;
-        areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
-        // (unused here; a constant, so that the register sets of the two
-        // weight sources never merge with a register a load is still
-        // filling, which would make the compiler wait for every load)
-        areg[set][1] = make_uint4(0, 0, 0, 0);
-      }
+      // Both weight sources issue the same two loads (the int8 codes need
+      // only the first; their second reads past the buffer and returns
+      // zeros, with no memory access), so a register set is only ever
+      // written by loads. Written by a load on one source and a constant on
+      // the other, the second half made the compiler wait for every load in
+      // flight before each step's constant, which left one stage of loads
+      // in flight instead of four.
+      const int off0 = wide ? (ok ? (ra * K + col) * 2 : 0x7fffffe0) : (ok ? ra * K + col : 0x7fffffe0);
+      const int off1 = wide ? off0 + 16 : 0x7ffffff0;
+      areg[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off0, 0, 0));
+      areg[set][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off1, 0, 0));
     };
     // token side: wave w fills token rows w * 32 + 16 p + lane / 4
     const int rows_b = (int)min<int64_t>(BM, M - m0);
@@ -678,11 +677,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 #pragma unroll
       for (int r = 0; r < Cfg::NREADS; ++r) read_one(base, r, fset);
     };
-    // loads per step: the weight registers (one or two), the token DMA
-    // (DLB); stage st+1's are followed by those of stages st+2 and st+3
-    auto wait_next = [&]() {
-      if (wide) wait_vmcnt<2 * (2 + DLB)>(); else wait_vmcnt<2 * (1 + DLB)>();
-    };
+    // loads per step: the two weight register loads, the token DMA (DLB);
+    // stage st+1's are followed by those of stages st+2 and st+3
+    auto wait_next = [&]() { wait_vmcnt<2 * (2 + DLB)>(); };
     // With one wave per SIMD (the 128 x 128 tiles) the fragments of stage
     // st+1 are read while the MFMAs of stage st run (two register sets);
     // with two (the 256 x 256 tiles) the other wave covers the reads, and a
@@ -723,7 +720,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     }
     w_cur = word_of(0);
     w_next = word_of(1);
-    if (wide) wait_vmcnt<3 * (2 + DLB)>(); else wait_vmcnt<3 * (1 + DLB)>();
+    wait_vmcnt<3 * (2 + DLB)>();
     write_a(0, 0, w_cur);
     lds_barrier();
     if constexpr (DBF)
