@@ -368,7 +368,7 @@ def test_linear_edge_cases(gpu, case):
 
 @pytest.mark.parametrize("case", ["n17", "n33", "n70", "n100", "all_columns", "large_tiles_n40",
                                   "large_tiles_all", "wide_all", "n600", "block_run",
-                                  "tail_block"])
+                                  "tail_block", "chunks3_all"])
 def test_linear_many_outliers(gpu, case):
     """More than 16 outlier columns, three workspaces: the minimal one, the
     default region of recovered weights (workspace_bytes(M, K, N), room for
@@ -380,7 +380,10 @@ def test_linear_many_outliers(gpu, case):
     in the epilogue. Without room the GEMM's dense second loop runs over all
     K columns (all columns outliers: the int8 loop is skipped). Every Y within
     the tolerance of the oracle. wide_all: N * LD(K) / 8 = 1.07M 16-byte
-    pieces, more than one pass of the recovery's grid. block_run and
+    pieces, more than one pass of the recovery's grid. chunks3_all: rows of
+    three 2048-column chunks on a grid of 2048 blocks, so a block's chunk
+    changes from task to task (96 tokens: at most 64 the few-token kernel
+    takes the layer and no weights are recovered). block_run and
     tail_block make whole 64-column k-blocks outlier columns (ten in a row;
     the partial last block), which the int8 loop of the segment modes skips:
     their codes are all zero, so the int32 sums, and Y against the step
@@ -389,7 +392,7 @@ def test_linear_many_outliers(gpu, case):
     rng = np.random.default_rng(300 + len(case))
     large = case.startswith("large_tiles")
     M, K, N = (4100, 528, 4100) if large else (300, 2064, 4100) if case in ("wide_all", "n600") \
-        else (200, 1040, 300)
+        else (96, 4224, 2100) if case == "chunks3_all" else (200, 1040, 300)
     X = synth.normal_f16(rng, (M, K), 1.0)
     W = synth.normal_f16(rng, (N, K), 0.05)
     tau = 6.0
