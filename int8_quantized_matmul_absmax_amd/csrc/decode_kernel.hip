@@ -55,6 +55,7 @@
 
 #include <atomic>
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launchers.h"
@@ -110,6 +111,72 @@ __device__ __forceinline__ uint2 dc_codes8(const uint4& t, float s) {
                     __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
 }
 
+// Maxima over the 64 lanes of a wave of V values per lane, all V at once.
+// Each step pairs every lane with a partner and, while more than one value
+// is left, halves the values a lane holds: by one lane bit it keeps the
+// lower or the upper half and takes its partner's copy of the same half
+// (V - 1 exchanges in all, where V separate reductions take 6 V). The
+// pairings: lanes i and i ^ 32 (v_permlane32_swap), i and i ^ 16
+// (v_permlane16_swap), then within each 16-lane row i and 15 - i
+// (row_mirror), i and 7 - i within each 8 (row_half_mirror), i and i ^ 2,
+// i and i ^ 1 (quad_perm). The halving steps take lane bits 5, 4, 3, 2 in
+// that order; each later pairing keeps those bits (the mirrors flip only
+// lower ones), so partners always hold the same values, and the lanes each
+// step adds are new. Once one value is left the steps are plain maxima.
+// Afterwards lane (64 / V) * r (and the lanes up to the next such one)
+// holds the maximum of value r.
+template <int V>
+__device__ __forceinline__ void wave_max_transposed(uint32_t (&v)[V], int lane) {
+  static_assert(V == 1 || V == 2 || V == 4 || V == 8 || V == 16, "values per lane");
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  constexpr int H1 = V / 2, H2 = V / 4, H3 = V / 8, H4 = V / 16;   // halves per step (0: plain)
+  // lanes i and i ^ 32: after the swap the first result holds (own, partner)
+  // of the lower value at the lower lanes, the second (partner, own) of the
+  // upper value at the upper lanes
+  if constexpr (H1 > 0) {
+#pragma unroll
+    for (int k = 0; k < H1; ++k) {
+      const auto p = __builtin_amdgcn_permlane32_swap(v[k], v[k + H1], false, false);
+      v[k] = umax(p[0], p[1]);
+    }
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(v[0], v[0], false, false);
+    v[0] = umax(p[0], p[1]);
+  }
+  // lanes i and i ^ 16, the same way on 16-lane rows
+  if constexpr (H2 > 0) {
+#pragma unroll
+    for (int k = 0; k < H2; ++k) {
+      const auto p = __builtin_amdgcn_permlane16_swap(v[k], v[k + H2], false, false);
+      v[k] = umax(p[0], p[1]);
+    }
+  } else {
+    const auto p = __builtin_amdgcn_permlane16_swap(v[0], v[0], false, false);
+    v[0] = umax(p[0], p[1]);
+  }
+  // within 16 lanes through DPP: a halving step keeps half h by lane bit g
+  // and sends the other half to the partner
+  auto dpp_step = [&](auto ctrl_c, int g, auto h_c) __attribute__((always_inline)) {
+    constexpr int ctrl = decltype(ctrl_c)::value, h = decltype(h_c)::value;
+    if constexpr (h > 0) {
+      const bool up = (lane >> g) & 1;
+#pragma unroll
+      for (int k = 0; k < h; ++k) {
+        const uint32_t keep = up ? v[k + h] : v[k];
+        const uint32_t send = up ? v[k] : v[k + h];
+        v[k] = umax(keep, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, ctrl, 0xf, 0xf, false));
+      }
+    } else {
+      v[0] = umax(v[0], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[0], ctrl, 0xf, 0xf, false));
+    }
+  };
+  using ic = std::integral_constant<int, 0>;
+  dpp_step(std::integral_constant<int, 0x140>{}, 3, std::integral_constant<int, H3>{});   // row_mirror
+  dpp_step(std::integral_constant<int, 0x141>{}, 2, std::integral_constant<int, H4>{});   // row_half_mirror
+  dpp_step(std::integral_constant<int, 0x4e>{}, 0, ic{});   // quad_perm [2,3,0,1]
+  dpp_step(std::integral_constant<int, 0xb1>{}, 0, ic{});   // quad_perm [1,0,3,2]
+}
+
 // LDS row pitch of the int8 codes: K rounded up to 256 bytes, plus 16, so
 // the 16 token rows of one fragment read hit distinct banks.
 __host__ __device__ constexpr int dc_pitch(int K) { return (K + 255) / 256 * 256 + kDcPad; }
@@ -120,8 +187,9 @@ __host__ __device__ constexpr int dc_lds_bytes(int M, int K) {
 }
 
 // X thread t holds the 16-byte chunks t, t + 512, ... (JC of them, K <= JC *
-// 4096) of each of the first MR token rows (M <= MR, MR * JC <= kDcXRegs).
-template <int MR, int JC>
+// 4096) of each of the first MR token rows (M <= MR, MR * JC <= kDcXRegs);
+// FULL: M == MR, so no loop over the rows needs a bound.
+template <int MR, int JC, bool FULL>
 __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     const uint16_t* __restrict__ X, const int8_t* __restrict__ Wq, const float* __restrict__ sw,
     int M, int N, int K, uint32_t tau16, const uint16_t* __restrict__ bias,
@@ -272,7 +340,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     for (int i = 0; i < 4; ++i) mx[i] = u16x2{0, 0};
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      if (m < M) {
+      if (FULL || m < M) {
         const uint32_t w[4] = {xr[m][j].x, xr[m][j].y, xr[m][j].z, xr[m][j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -316,9 +384,12 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       bmk[j][h] = k;
     }
   }
+  // the row maxima of all MR rows reduced over the wave together (rows past
+  // M hold a copy of row M - 1, from the clamped loads, and are not read)
+  {
+    uint32_t rv[MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (m < M) {
+    for (int m = 0; m < MR; ++m) {
       u16x2 m2 = u16x2{0, 0};
 #pragma unroll
       for (int j = 0; j < JC; ++j) {
@@ -327,9 +398,11 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
         for (int i = 0; i < 4; ++i)
           m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & amk[j][i]));
       }
-      const uint32_t mxw = wave_max_u32_dpp(m2[0] > m2[1] ? m2[0] : m2[1]);
-      if (lane == 0) s_rmax[xw][m] = mxw;
+      rv[m] = m2[0] > m2[1] ? m2[0] : m2[1];
     }
+    wave_max_transposed<MR>(rv, lane);
+    constexpr int kStride = kWave / MR;   // lane kStride * r holds row r
+    if ((lane & (kStride - 1)) == 0) s_rmax[xw][lane / kStride] = rv[0];
   }
   // the X waves' exchange: each arrives once its LDS writes are done, and
   // waits until all eight have (every X wave reaches each exchange; the
@@ -373,16 +446,18 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     sc_l = a != 0.0f ? 127.0f / a : 0.0f;
     if (xw == 0) s_sx[lane] = a;
   }
+  float scm[MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (m < M) {
-      const float sc = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), m));
+  for (int m = 0; m < MR; ++m)
+    scm[m] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), m));
 #pragma unroll
-      for (int j = 0; j < JC; ++j) {
-        const int c = xt + kDcXThreads * j;
-        if (c < nchunks) {
-          uint2 q = dc_codes8(xr[m][j], sc);
+  for (int j = 0; j < JC; ++j) {
+    const int c = xt + kDcXThreads * j;
+    if (c < nchunks) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (FULL || m < M) {
+          uint2 q = dc_codes8(xr[m][j], scm[m]);
           q.x &= bmk[j][0];
           q.y &= bmk[j][1];
           *reinterpret_cast<uint2*>(s_xq + m * ldx + c * 8) = q;
@@ -412,7 +487,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
         else if (first) cols_g[pos] = col;   // (more than fit in LDS)
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          if (m < M) {
+          if (FULL || m < M) {
             const uint16_t v = (uint16_t)pick_half(xr[m][j], e);
             if (pos < kDcMaxOut) s_xo[m][pos] = v;
             else if (first) Xo_g[m * ld + pos] = v;
@@ -551,7 +626,7 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
 constexpr int kDcMaxDevices = 64;
 std::atomic<int> g_cus[kDcMaxDevices];
 
-template <int MR, int JC>
+template <int MR, int JC, bool FULL>
 hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw, int64_t M,
                            int64_t N, int64_t K, uint32_t tau16, const uint16_t* bias,
                            uint16_t* Y, const uint16_t* Wf, uint32_t* bitmap, int32_t* cols,
@@ -564,7 +639,7 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
   // per instantiation and device: allow the largest dynamic LDS once
   static std::atomic<bool> lds_set[kDcMaxDevices];
   if (!lds_set[slot].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_i8<MR, JC>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_i8<MR, JC, FULL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             dc_lds_bytes(MR, JC * kDcXThreads * 8));
     if (e != hipSuccess) return e;
@@ -581,7 +656,7 @@ hipError_t launch_decode_t(const uint16_t* X, const int8_t* Wq, const float* sw,
   // first round take further tiles in turn
   const int64_t tiles = (N + kDcFeat - 1) / kDcFeat;
   const int64_t blocks = std::min<int64_t>(tiles, cus);
-  hipLaunchKernelGGL((k_decode_i8<MR, JC>), dim3((unsigned)blocks), dim3(kDcThreads), (size_t)lds,
+  hipLaunchKernelGGL((k_decode_i8<MR, JC, FULL>), dim3((unsigned)blocks), dim3(kDcThreads), (size_t)lds,
                      s, X, Wq, sw, (int)M, (int)N, (int)K, tau16, bias, Y, Wf, bitmap, cols,
                      n_out, sx, Xq, Xo);
   return hipGetLastError();
@@ -607,24 +682,30 @@ hipError_t launch_decode(const uint16_t* X, const int8_t* Wq, const float* sw, i
   if (N <= 0) return hipSuccess;
   // chunks per row per X thread
   const int64_t jc = (K + kDcXThreads * 8 - 1) / (kDcXThreads * 8);
-#define I8MM_DECODE(MR_, JC_)                                                                   \
-  return launch_decode_t<MR_, JC_>(X, Wq, sw, M, N, K, tau16, bias, Y, Wf, bitmap, cols, n_out, \
-                                   sx, Xq, Xo, s)
+#define I8MM_DECODE(MR_, JC_, FULL_)                                                        \
+  return launch_decode_t<MR_, JC_, FULL_>(X, Wq, sw, M, N, K, tau16, bias, Y, Wf, bitmap, cols, \
+                                          n_out, sx, Xq, Xo, s)
+#define I8MM_DECODE_MR(MR_, JC_)            \
+  do {                                      \
+    if (M == MR_) I8MM_DECODE(MR_, JC_, true); \
+    I8MM_DECODE(MR_, JC_, false);           \
+  } while (0)
   if (M == 1) {
-    if (jc <= 1) I8MM_DECODE(1, 1);
-    if (jc <= 2) I8MM_DECODE(1, 2);
-    I8MM_DECODE(1, 4);
+    if (jc <= 1) I8MM_DECODE(1, 1, true);
+    if (jc <= 2) I8MM_DECODE(1, 2, true);
+    I8MM_DECODE(1, 4, true);
   }
   if (M <= 4) {
-    if (jc <= 1) I8MM_DECODE(4, 1);
-    if (jc <= 2) I8MM_DECODE(4, 2);
-    I8MM_DECODE(4, 4);
+    if (jc <= 1) I8MM_DECODE_MR(4, 1);
+    if (jc <= 2) I8MM_DECODE_MR(4, 2);
+    I8MM_DECODE_MR(4, 4);
   }
   if (M <= 8) {
-    if (jc <= 1) I8MM_DECODE(8, 1);
-    I8MM_DECODE(8, 2);
+    if (jc <= 1) I8MM_DECODE_MR(8, 1);
+    I8MM_DECODE_MR(8, 2);
   }
-  I8MM_DECODE(16, 1);
+  I8MM_DECODE_MR(16, 1);
+#undef I8MM_DECODE_MR
 #undef I8MM_DECODE
 }
 
