@@ -355,13 +355,12 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     }
     om[j] = c < nchunks ? mask : 0u;
     uint32_t word = om[j] << (8 * (c & 3));
-    word |= (uint32_t)__shfl_xor((int)word, 1, kWave);
-    word |= (uint32_t)__shfl_xor((int)word, 2, kWave);
+    word = quad_or_dpp(word);
     if ((c & 3) == 0 && c < nchunks) {
       sbm[c >> 2] = word;
     }
     const int cnt = __popc(om[j]);
-    const int incl = wave_inclusive_scan(cnt, lane);
+    const int incl = wave_inclusive_scan_dpp(cnt);
     excl[j] = incl - cnt;
     if (lane == kWave - 1) s_cnt[xw][j] = incl;
   }
@@ -483,15 +482,16 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
       for (uint32_t bits = om[j]; bits; bits &= bits - 1u) {
         const int e = __builtin_ctz(bits);
         const int col = c * 8 + e;
-        if (pos < kDcMaxOut) s_cols[pos] = col;
-        else if (first) cols_g[pos] = col;   // (more than fit in LDS)
+        if (pos < kDcMaxOut) {
+          s_cols[pos] = col;
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          if (FULL || m < M) {
-            const uint16_t v = (uint16_t)pick_half(xr[m][j], e);
-            if (pos < kDcMaxOut) s_xo[m][pos] = v;
-            else if (first) Xo_g[m * ld + pos] = v;
-          }
+          for (int m = 0; m < MR; ++m)
+            if (FULL || m < M) s_xo[m][pos] = (uint16_t)pick_half(xr[m][j], e);
+        } else if (first) {   // (more than fit in LDS)
+          cols_g[pos] = col;
+#pragma unroll
+          for (int m = 0; m < MR; ++m)
+            if (FULL || m < M) Xo_g[m * ld + pos] = (uint16_t)pick_half(xr[m][j], e);
         }
         ++pos;
       }

@@ -71,6 +71,27 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
   return a > b ? a : b;
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP adds (no LDS round trips):
+// within each 16-lane row by row_shr 1, 2, 4, 8 (lanes shifted in read 0),
+// then row 0's last lane is added to row 1 and row 2's to row 3
+// (row_bcast:15), and lane 31's total to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return v;
+}
+
+// OR over the four lanes of each quad (quad_perm [1,0,3,2], then [2,3,0,1]).
+__device__ __forceinline__ uint32_t quad_or_dpp(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false);
+  return v;
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
