@@ -91,8 +91,11 @@ __host__ __device__ constexpr int dc_round16(int v) { return (v + 15) / 16 * 16;
 // with ties to even and its low byte is the two's complement code. The
 // product is taken as fma(x, s, +0), one mixed-precision instruction that
 // reads the fp16 half directly: x * s is exact before its one rounding
-// either way, and a -0 product becoming +0 does not change the code.
-__device__ __forceinline__ uint2 dc_codes8(const uint4& t, float s) {
+// either way, and a -0 product becoming +0 does not change the code. The
+// last two byte permutes take their selectors from the caller (0x05040100
+// keeps all four codes of a word; a selector byte 0x0c writes a zero code).
+__device__ __forceinline__ uint2 dc_codes8(const uint4& t, float s, uint32_t sel_x,
+                                           uint32_t sel_y) {
   const float magic = 12582912.0f;
   const uint32_t w[4] = {t.x, t.y, t.z, t.w};
   uint32_t r[8];
@@ -107,8 +110,8 @@ __device__ __forceinline__ uint2 dc_codes8(const uint4& t, float s) {
   const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u);
   const uint32_t hi01 = __builtin_amdgcn_perm(r[5], r[4], 0x0c0c0400u);
   const uint32_t hi23 = __builtin_amdgcn_perm(r[7], r[6], 0x0c0c0400u);
-  return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                    __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+  return make_uint2(__builtin_amdgcn_perm(lo23, lo01, sel_x),
+                    __builtin_amdgcn_perm(hi23, hi01, sel_y));
 }
 
 // Maxima over the 64 lanes of a wave of V values per lane, all V at once.
@@ -365,8 +368,9 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     if (lane == kWave - 1) s_cnt[xw][j] = incl;
   }
   // per chunk: the magnitude bits of its normal elements (outlier elements
-  // and sign bits cleared), and byte masks that clear the outlier codes
-  uint32_t amk[JC][4], bmk[JC][2];
+  // and sign bits cleared), and the code-packing selectors that write zero
+  // codes at the outlier elements
+  uint32_t amk[JC][4], bsel[JC][2];
 #pragma unroll
   for (int j = 0; j < JC; ++j) {
     const bool cv = xt + kDcXThreads * j < nchunks;   // not a clamped chunk
@@ -377,10 +381,11 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t k = 0;
+      uint32_t k = 0x05040100u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) k |= ((om[j] >> (4 * h + e)) & 1u) ? 0u : 0xffu << (8 * e);
-      bmk[j][h] = k;
+      for (int e = 0; e < 4; ++e)
+        if ((om[j] >> (4 * h + e)) & 1u) k = (k & ~(0xffu << (8 * e))) | (0x0cu << (8 * e));
+      bsel[j][h] = k;
     }
   }
   // the row maxima of all MR rows reduced over the wave together (rows past
@@ -455,12 +460,9 @@ __global__ __launch_bounds__(kDcThreads) void k_decode_i8(
     if (c < nchunks) {
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        if (FULL || m < M) {
-          uint2 q = dc_codes8(xr[m][j], scm[m]);
-          q.x &= bmk[j][0];
-          q.y &= bmk[j][1];
-          *reinterpret_cast<uint2*>(s_xq + m * ldx + c * 8) = q;
-        }
+        if (FULL || m < M)
+          *reinterpret_cast<uint2*>(s_xq + m * ldx + c * 8) =
+              dc_codes8(xr[m][j], scm[m], bsel[j][0], bsel[j][1]);
       }
     }
   }

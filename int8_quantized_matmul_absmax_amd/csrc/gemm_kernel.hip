@@ -182,8 +182,11 @@ __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm,
 //            outlier product as a second main-loop segment.
 //   kDenseSeg  more than 16 outlier columns, X given, and Wo not given or
 //            without room for them (returns at once otherwise): the
-//            outlier product as a dense second segment over all K columns.
-enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2, kDenseSeg = 3 };
+//            outlier product as a dense second segment over all K columns,
+//            the weight columns recovered from Wq in the loop.
+//   kDenseSegW  kDenseSeg with the weight kept in fp16 (Wf), launched
+//            instead of it when Wf is given.
+enum GemmMode { kPlain = 0, kInt32 = 1, kOutlierSeg = 2, kDenseSeg = 3, kDenseSegW = 4 };
 template <class Cfg, int MODE>
 __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, const float* __restrict__ sx,
@@ -232,10 +235,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   const bool dense_case = n_o > 16 && !compact && Xd != nullptr && bmp != nullptr;
   // each mode returns at once when the case is another mode's
   if (MODE == kOutlierSeg && !compact) return;
-  if (MODE == kDenseSeg && !dense_case) return;
+  if ((MODE == kDenseSeg || MODE == kDenseSegW) && !dense_case) return;
   if ((MODE == kPlain || MODE == kInt32) && (compact || dense_case)) return;
-  constexpr bool seg2 = MODE == kOutlierSeg || MODE == kDenseSeg;
-  constexpr bool dense = MODE == kDenseSeg;
+  constexpr bool seg2 = MODE == kOutlierSeg || MODE == kDenseSeg || MODE == kDenseSegW;
+  constexpr bool dense = MODE == kDenseSeg || MODE == kDenseSegW;
   uint16_t* s_wo = reinterpret_cast<uint16_t*>(lds + Cfg::OUTL0);   // [BN][16]
   uint16_t* s_xo = s_wo + BN * 16;                                  // [BM][16]
   // Values held in registers from the prologue to the end of the main loop
@@ -572,12 +575,13 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const int S = (K + 31) / 32;
     // bitmap word of stage st (0 past the last stage): a scalar load
     auto word_of = [&](int st) -> uint32_t {
-      return st < S ? __builtin_amdgcn_readfirstlane(bmp[st]) : 0u;
+      const uint32_t w = __builtin_amdgcn_readfirstlane(bmp[st < S ? st : S - 1]);
+      return st < S ? w : 0u;
     };
     // weight side: row ra, columns 16 * hf .. of each stage
     const int ra = tid >> 1, hf = tid & 1;
     const int rows_a = (int)min<int64_t>(BN, N - n0);
-    const bool wide = Wf != nullptr;   // fp16 weight: 32 bytes a thread
+    constexpr bool wide = MODE == kDenseSegW;   // fp16 weight: 32 bytes a thread
     const __amdgpu_buffer_rsrc_t rsa = wide
         ? make_rsrc(Wf + n0 * K, (uint32_t)rows_a * (uint32_t)K * 2u)
         : make_rsrc(Wq + n0 * K, (uint32_t)rows_a * (uint32_t)K);
@@ -645,10 +649,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
       const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - k;
       return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     };
-    auto write_a = [&](int st, int set, uint32_t word) {
+    // The converted fp16 weights of one register set: 16 columns of the
+    // thread's row, non-outlier columns zeroed (W: the weight is kept in
+    // fp16). The byte mask (0xff where a column is an outlier column) comes
+    // from a byte permute whose selector bytes are 0x0c (a zero byte) or 0x0d
+    // (0xff): two full-rate operations instead of a quarter-rate multiply.
+    auto convert_a = [&](int set, uint32_t word, uint32_t (&h)[8]) __attribute__((always_inline)) {
       const uint32_t bits = (word >> (16 * hf)) & 0xffffu;   // outlier columns of the 16
-      uint32_t h[8];
-      if (wide) {
+      if constexpr (wide) {
         const uint32_t w8[8] = {areg[set][0].x, areg[set][0].y, areg[set][0].z, areg[set][0].w,
                                 areg[set][1].x, areg[set][1].y, areg[set][1].z, areg[set][1].w};
 #pragma unroll
@@ -661,15 +669,23 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t b4 = (bits >> (4 * i)) & 15u;
-          const uint32_t keep = ((b4 * 0x00204081u) & 0x01010101u) * 0xffu;
+          const uint32_t m1 = (b4 * 0x00204081u) & 0x01010101u;
+          const uint32_t keep = __builtin_amdgcn_perm(0u, 0u, 0x0c0c0c0cu | m1);
           const uint2 c = cvt4(w4[i] & keep);
           h[2 * i] = c.x;
           h[2 * i + 1] = c.y;
         }
       }
+    };
+    auto store_a = [&](int st, const uint32_t (&h)[8]) __attribute__((always_inline)) {
       int8_t* row = stages + (st % DNB) * Cfg::STAGE_BYTES + ra * BK;
       lds_store16(row + (((2 * hf) ^ key_a) << 4), h[0], h[1], h[2], h[3]);
       lds_store16(row + (((2 * hf + 1) ^ key_a) << 4), h[4], h[5], h[6], h[7]);
+    };
+    auto write_a = [&](int st, int set, uint32_t word) {
+      uint32_t h[8];
+      convert_a(set, word, h);
+      store_a(st, h);
     };
     const std::integral_constant<bool, true> f16{};
     auto read_stage = [&](int st, int fset) {
@@ -689,20 +705,42 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     // q: the register set of stage st+4 (= st mod 4); fragment set of stage
     // st: st mod 2
     uint32_t w_cur = 0, w_next = 0;   // bitmap words of stages st, st+1
+    // With the double-buffered fragments (one wave per SIMD), every step runs
+    // all of stage st's MFMAs, a stage without outlier columns included (its
+    // converted weights are zeros and add nothing: an accumulator that is
+    // +0 or nonzero is unchanged by zero products, and none is ever -0), so
+    // the step is one branch-free block: the first half of the MFMAs is
+    // interleaved with the weight conversion of stage st+1, one MFMA then a
+    // few VALU operations, and the matrix pipe runs while the wave converts;
+    // the rest go with the fragment reads of stage st+1 after the barrier.
+    constexpr int PRE = Cfg::NMFMA / 2;
     auto dstep = [&](int st, auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
       wait_next();
-      write_a(st + 1, (q + 1) & 3, w_next);
+      if constexpr (DBF) {
+#pragma unroll
+        for (int m = 0; m < PRE; ++m) mfma_one(m, q & 1, f16);
+        uint32_t h[8];
+        convert_a((q + 1) & 3, w_next, h);
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then VALU
+        }
+        store_a(st + 1, h);
+      } else {
+        uint32_t h[8];
+        convert_a((q + 1) & 3, w_next, h);
+        store_a(st + 1, h);
+      }
       lds_barrier();
       load_a(st + 4, q);
       load_b(st + 4);
       const uint32_t w_after = word_of(st + 2);
       if constexpr (DBF) {
-        if (w_next) read_stage(st + 1, (q + 1) & 1);
-        if (w_cur) {
+        read_stage(st + 1, (q + 1) & 1);
 #pragma unroll
-          for (int m = 0; m < Cfg::NMFMA; ++m) mfma_one(m, q & 1, f16);
-        }
+        for (int m = PRE; m < Cfg::NMFMA; ++m) mfma_one(m, q & 1, f16);
       } else {
         if (w_cur) {
           read_stage(st, 0);
@@ -723,8 +761,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     wait_vmcnt<3 * (2 + DLB)>();
     write_a(0, 0, w_cur);
     lds_barrier();
-    if constexpr (DBF)
-      if (w_cur) read_stage(0, 0);
+    if constexpr (DBF) read_stage(0, 0);
     const std::integral_constant<int, 0> q0{};
     const std::integral_constant<int, 1> q1{};
     const std::integral_constant<int, 2> q2{};
@@ -1061,9 +1098,14 @@ hipError_t launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* sx, co
   if (Xd && bmp) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_i8<Cfg, kDenseSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
-                       (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp,
-                       kbl);
+    if (Wf)
+      hipLaunchKernelGGL((k_gemm_i8<Cfg, kDenseSegW>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
+                         (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp,
+                         kbl);
+    else
+      hipLaunchKernelGGL((k_gemm_i8<Cfg, kDenseSeg>), grid, block, 0, s, Xq, Wq, sx, sw, (int)M,
+                         (int)N, (int)K, Xo, cols, n_out, bias, Y, C, Wo, wo_cols, Wf, Xd, bmp,
+                         kbl);
   }
   return hipGetLastError();
 }
