@@ -696,15 +696,16 @@ def _short(name):
 def _family(name):
     """Kernel family of a dispatch: the kernel's name without its template
     arguments, except the GEMM's two segment modes (its last template
-    argument: 2 the compact outlier segment, 3 the dense one), which are
-    listed apart: the layer launches the plain mode and a segment mode, and
-    the one whose case it is not returns at once; other kernels (the copy
-    probe) by what they are."""
+    argument: 2 the compact outlier segment, 3 and 4 the dense one, with
+    the weight as int8 codes or kept in fp16), which are listed apart: the
+    layer launches the plain mode and a segment mode, and the one whose case
+    it is not returns at once; other kernels (the copy probe) by what they
+    are."""
     s = _short(name)
     if s.startswith("k_gemm_i8"):
         if re.search(r",\s*2>$", s):
             return "k_gemm_i8_outlier_seg"
-        if re.search(r",\s*3>$", s):
+        if re.search(r",\s*[34]>$", s):
             return "k_gemm_i8_dense_seg"
         return "k_gemm_i8"
     return s.split("<")[0] if s.startswith("k_") else ("copy" if "copy" in name.lower() else s)
