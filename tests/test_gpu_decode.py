@@ -46,6 +46,10 @@ CASES = {
     "m10_k8192_separate": (10, 8192, 300, 12, False, False),
     "m13_k4096_n40": (13, 4096, 1000, 40, False, False),
     "m1_k16384": (1, 16384, 700, 9, True, False),
+    "m2_k8192_n7": (2, 8192, 300, 7, True, False),
+    "m10_k4096_n6": (10, 4096, 400, 6, False, False),
+    "m11_k4096_n6": (11, 4096, 400, 6, False, False),
+    "m1_k4096_n15_many_tiles": (1, 4096, 16400, 15, True, False),
 }
 
 
