@@ -558,8 +558,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
   // itself) with the normal columns zeroed (bitmap word of the stage), and
   // writes them to LDS. The token rows are X itself, by DMA: X is finite on
   // the normal columns (a column holding inf or NaN is an outlier column),
-  // so the zeroed weights remove them exactly. A stage whose bitmap word is 0
-  // issues no fragment reads and no MFMA.
+  // so the zeroed weights remove them exactly. On the 256 x 256 tiles a stage
+  // whose bitmap word is 0 issues no fragment reads and no MFMA; on the
+  // 128 x 128 tiles every stage runs them (see the step below).
   // Step st: stage st+1's loads have landed; its weights go to LDS; barrier
   // (stage st+1 visible to every wave; every wave is done reading stage st);
   // the loads of stage st+4 (registers: set (st+4) % 4; DMA: the buffer of
@@ -767,7 +768,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_i8(
     const std::integral_constant<int, 2> q2{};
     const std::integral_constant<int, 3> q3{};
     // in fours (steps past the last stage find zeros and a bitmap word of
-    // 0: no reads, no MFMAs), so the register sets stay where they are
+    // 0, so their MFMAs add nothing), so the register sets stay where they
+    // are
     for (int st = 0; st < S; st += 4) {
       dstep(st, q0);
       dstep(st + 1, q1);
