@@ -456,7 +456,13 @@ __global__ __launch_bounds__(256) void k_rows(const uint16_t* __restrict__ X, in
 // the codes are stored chunk by chunk. Loads and stores are buffer
 // operations over the row (the chunk offset in the scalar operand), so a
 // chunk past the row reads 0 and its store is dropped. Arithmetic as k_rows.
-template <int CPB, int FMODE>
+// STG: the row's Xo is assembled in LDS (a buffer of ld_max elements per row
+// parity, after the bitmap words) and written after the row's barrier as
+// aligned 16-byte stores, zeros past n included. Written straight to memory,
+// a chunk's outlier elements land at positions that are multiples of 8 only
+// by chance when most columns are outlier columns, and then go out as 2-byte
+// stores, one per element.
+template <int CPB, int FMODE, bool STG>
 __global__ __launch_bounds__(256) void k_rows_flagged(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ flags,
     int bands, uint32_t* __restrict__ bitmap_out, int8_t* __restrict__ Xq,
@@ -472,6 +478,9 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
   const int64_t nchunks = K / 8;
   uint32_t* sbm = smem;
   uint32_t* spre = smem + nwords;
+  // STG only: 16-byte aligned, after the bitmap words and their prefix
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem + (2 * nwords + 3) / 4 * 4);
+  const int64_t ld_max = (K + 31) / 32 * 32;
   const int64_t row0 = blockIdx.x, rstep = gridDim.x;
 
   // flag words first, then the first row: waiting for the flags leaves the
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
           if (Xo) {
             const int64_t k0 = (tid + (int64_t)j * kRowThreads) * 8;
             int pos = (int)spre[k0 >> 5] + __popc(sbm[k0 >> 5] & ((1u << (k0 & 31)) - 1u));
-            uint16_t* dst = Xo + row * ld;
+            uint16_t* dst = STG ? stage + parity * ld_max : Xo + row * ld;
             if (om == 0xffu && (pos & 7) == 0) {
               st16(dst + pos, v[j]);   // 8 outlier columns at 8 aligned positions
             } else {
@@ -593,8 +602,29 @@ __global__ __launch_bounds__(256) void k_rows_flagged(
       }
       if (tid == 0) sx[row] = a;
     }
-    if (Xo)
-      for (int64_t t = n + tid; t < ld; t += kRowThreads) Xo[row * ld + t] = 0;
+    if (Xo) {
+      if constexpr (STG) {
+        // the row's Xo from LDS, 8 elements a thread, zeros past n
+        const uint16_t* st = stage + parity * ld_max;
+        for (int64_t t = (int64_t)tid * 8; t < ld; t += kRowThreads * 8) {
+          uint4 w = make_uint4(0u, 0u, 0u, 0u);
+          if (t < n) {
+            w = *reinterpret_cast<const uint4*>(st + t);
+            const int64_t valid = n - t;   // elements of the chunk below n
+            if (valid < 8) {
+              uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                ww[i] &= (2 * i < valid ? 0xffffu : 0u) | (2 * i + 1 < valid ? 0xffff0000u : 0u);
+              w = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+            }
+          }
+          st16(Xo + row * ld + t, w);
+        }
+      } else {
+        for (int64_t t = n + tid; t < ld; t += kRowThreads) Xo[row * ld + t] = 0;
+      }
+    }
   };
 
   // two rows per iteration, alternating register sets (static indices)
@@ -616,10 +646,20 @@ hipError_t launch_rows_flagged_t(const uint16_t* X, int64_t M, int64_t K, const 
                                  uint16_t* Xo, int32_t* cols, int32_t* n_out, int32_t* kbl,
                                  hipStream_t s) {
   const int nwords = (int)((K + 31) / 32);
-  const size_t shm = (size_t)nwords * 2 * sizeof(uint32_t);
+  size_t shm = (size_t)nwords * 2 * sizeof(uint32_t);
   // four resident blocks per CU on 256 CUs; each block walks its rows
   const int64_t blocks = std::min<int64_t>(M, 1024);
-  auto kern = bands == 1 ? k_rows_flagged<CPB, kBitmap> : k_rows_flagged<CPB, kBands>;
+  // Xo assembled in LDS for the widest rows only (the shapes whose many
+  // outlier columns made the direct stores the bound); one row buffer per
+  // register set in use (a block with one row uses one)
+  constexpr bool kStage = CPB == 8;
+  if (kStage && Xo)
+    shm = (size_t)((2 * nwords + 3) / 4 * 4) * sizeof(uint32_t) +
+          (size_t)(M > blocks ? 2 : 1) * (size_t)((K + 31) / 32 * 32) * 2;
+  auto kern = kStage && Xo ? (bands == 1 ? k_rows_flagged<CPB, kBitmap, kStage>
+                                         : k_rows_flagged<CPB, kBands, kStage>)
+                           : (bands == 1 ? k_rows_flagged<CPB, kBitmap, false>
+                                         : k_rows_flagged<CPB, kBands, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRowThreads), shm, s, X, M, K, flags,
                      bands, bitmap_out, Xq, sx, Xo, cols, n_out, kbl);
   return hipGetLastError();

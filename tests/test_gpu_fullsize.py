@@ -146,6 +146,12 @@ def test_mlp_sweep_per_layer(gpu, n_in):
     rows = sample_rows(M, 128, n_in)
     ref2 = O.linear_int8_mixed(G_ref, Wq2_ref, sw2_ref, 6.0, rows=rows)
     assert np.array_equal(host(v["Xq"])[rows], ref2["Xq"])
+    # the gathered outlier activations and their zero pad on the same rows
+    n2 = cols2.size
+    ld2 = (n2 + 31) // 32 * 32
+    Xo2 = host(v["Xo"])[: M * ld2].reshape(M, ld2)[rows].view(np.uint16)
+    assert np.array_equal(Xo2[:, :n2], G_ref[rows][:, cols2].view(np.uint16))
+    assert not Xo2[:, n2:].any()
     note("mlp n_in=%d layer 2 int32 accumulators on %d rows" % (n_in, rows.size))
     C2 = ops.int8_mm_dequant(v["Xq"], Wq2, v["sx"], sw2, want_y=False, want_int32=True)
     C2_s = host(C2[torch.from_numpy(rows).cuda()])
