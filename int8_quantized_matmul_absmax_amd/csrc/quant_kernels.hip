@@ -22,6 +22,8 @@
 
 #include <algorithm>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "i8mm.h"
 #include "launchers.h"
@@ -653,9 +655,31 @@ hipError_t launch_rows_flagged_t(const uint16_t* X, int64_t M, int64_t K, const 
   // outlier columns made the direct stores the bound); one row buffer per
   // register set in use (a block with one row uses one)
   constexpr bool kStage = CPB == 8;
-  if (kStage && Xo)
+  if (kStage && Xo) {
     shm = (size_t)((2 * nwords + 3) / 4 * 4) * sizeof(uint32_t) +
           (size_t)(M > blocks ? 2 : 1) * (size_t)((K + 31) / 32 * 32) * 2;
+    // up to 68 KB at K = 16384 (two row buffers), above the default limit
+    // of dynamic LDS: allowed once per device for both instantiations (the
+    // value is the same for every caller, so concurrent first calls are
+    // benign)
+    constexpr int kMaxDev = 64;
+    static std::atomic<bool> lds_set[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int slot = dev >= 0 && dev < kMaxDev ? dev : 0;
+    if (!lds_set[slot].load(std::memory_order_acquire)) {
+      const int max_words = (2 * ((2048 * CPB + 31) / 32) + 3) / 4 * 4;
+      const int max_bytes = max_words * (int)sizeof(uint32_t) + 2 * (2048 * CPB) * 2;
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rows_flagged<CPB, kBitmap, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_bytes);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rows_flagged<CPB, kBands, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, max_bytes);
+      if (e != hipSuccess) return e;
+      lds_set[slot].store(true, std::memory_order_release);
+    }
+  }
   auto kern = kStage && Xo ? (bands == 1 ? k_rows_flagged<CPB, kBitmap, kStage>
                                          : k_rows_flagged<CPB, kBands, kStage>)
                            : (bands == 1 ? k_rows_flagged<CPB, kBitmap, false>

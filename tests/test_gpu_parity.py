@@ -444,7 +444,7 @@ def test_linear_many_outliers(gpu, case):
 
 
 @pytest.mark.parametrize("case", ["clustered", "ragged_k", "sparse_words", "small_tiles_all",
-                                  "large_tiles_600", "wide_rows_many"])
+                                  "large_tiles_600", "wide_rows_many", "widest_rows_many"])
 def test_linear_dense_outlier_loop(gpu, case):
     """The GEMM's dense second loop (the workspace without the region of
     recovered weights): outlier columns clustered in a few 32-column words
@@ -454,14 +454,16 @@ def test_linear_dense_outlier_loop(gpu, case):
     with ragged M and N, and rows wider than 12288 with about 3000 outlier
     columns at unaligned positions over more token rows than row-pass
     blocks (the row pass then assembles Xo in LDS, two rows per block, with
-    an odd number of bitmap words). Intermediates bit for bit, Y within the tolerance;
+    an odd number of bitmap words, and at K = 16384, where its two row
+    buffers need more than 64 KB of LDS). Intermediates bit for bit, Y within the tolerance;
     with the int32 step call, the accumulators of the normal part bit for
     bit."""
     note("dense outlier loop %s" % case)
     rng = np.random.default_rng(640 + len(case))
     M, K, N = {"clustered": (300, 2048, 700), "ragged_k": (200, 1040, 330),
                "sparse_words": (130, 2048, 260), "small_tiles_all": (256, 1024, 384),
-               "large_tiles_600": (4100, 2064, 4100), "wide_rows_many": (1100, 13008, 64)}[case]
+               "large_tiles_600": (4100, 2064, 4100), "wide_rows_many": (1100, 13008, 64),
+               "widest_rows_many": (1100, 16384, 64)}[case]
     X = np.clip(synth.normal_f16(rng, (M, K), 1.0).astype(np.float32), -5.0, 5.0).astype(np.float16)
     tau = 6.0
     if case == "clustered":
@@ -472,7 +474,7 @@ def test_linear_dense_outlier_loop(gpu, case):
         cols = np.arange(5, K, 32)
     elif case == "small_tiles_all":
         cols, tau = np.arange(K), 0.0
-    elif case == "wide_rows_many":
+    elif case in ("wide_rows_many", "widest_rows_many"):
         cols = np.unique(np.concatenate([np.arange(96, 136), rng.choice(K, 3000, replace=False)]))
     else:
         cols = np.sort(rng.choice(K, 600, replace=False))
